@@ -1,0 +1,118 @@
+"""Pure-Python scalar-loop formulation of causal self-attention (oracle).
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring.  No numpy: nested
+lists of Python floats (IEEE double) and ``math.exp``/``math.log``, so it
+shares no vectorised primitive with :mod:`oracle.attention`.  Meant for tiny
+shapes (T <= 8); cost is O(T^2 D) Python operations per head.
+
+It follows the "Let's build GPT: from scratch, in code, spelled out" lecture
+description page: "version 1" walks over the past context with explicit
+loops; "version 3" turns masked affinities into weights with a softmax;
+"version 4" makes the affinities query-key dot products scaled by
+1/sqrt(head_size) (note 6 and the 01:20:05 correction); the 00:57:00
+correction fixes that only past and present positions are visible.
+
+Inputs are nested lists indexed ``[b][h][t][d]``; so are the outputs
+(``lse`` is ``[b][h][t]``).
+"""
+
+import math
+
+
+def _head_forward(q, k, v, scale):
+    T = len(q)
+    D = len(q[0])
+    o = []
+    lse = []
+    for i in range(T):
+        # affinities with keys 0..i only: the future is never looked at
+        s = []
+        for j in range(i + 1):
+            acc = 0.0
+            for d in range(D):
+                acc += q[i][d] * k[j][d]
+            s.append(scale * acc)
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        z = 0.0
+        for x in w:
+            z += x
+        row = []
+        for d in range(D):
+            acc = 0.0
+            for j in range(i + 1):
+                acc += w[j] * v[j][d]
+            row.append(acc / z)
+        o.append(row)
+        lse.append(m + math.log(z))
+    return o, lse
+
+
+def _head_backward(q, k, v, do, scale):
+    T = len(q)
+    D = len(q[0])
+    dq = [[0.0] * D for _ in range(T)]
+    dk = [[0.0] * D for _ in range(T)]
+    dv = [[0.0] * D for _ in range(T)]
+    for i in range(T):
+        s = []
+        for j in range(i + 1):
+            acc = 0.0
+            for d in range(D):
+                acc += q[i][d] * k[j][d]
+            s.append(scale * acc)
+        m = max(s)
+        w = [math.exp(x - m) for x in s]
+        z = 0.0
+        for x in w:
+            z += x
+        p = [x / z for x in w]
+        # o_i = sum_j p_ij v_j, so dL/dp_ij = do_i . v_j and dL/dv_j += p_ij do_i
+        g = []
+        for j in range(i + 1):
+            acc = 0.0
+            for d in range(D):
+                acc += do[i][d] * v[j][d]
+                dv[j][d] += p[j] * do[i][d]
+            g.append(acc)
+        # softmax: dL/ds_ij = p_ij (g_ij - sum_k p_ik g_ik)
+        mean = 0.0
+        for j in range(i + 1):
+            mean += p[j] * g[j]
+        for j in range(i + 1):
+            ds = p[j] * (g[j] - mean)
+            # s_ij = scale * q_i . k_j
+            for d in range(D):
+                dq[i][d] += scale * ds * k[j][d]
+                dk[j][d] += scale * ds * q[i][d]
+    return dq, dk, dv
+
+
+def forward(q, k, v, scale):
+    """Returns ``(o, lse)`` as nested lists."""
+    o, lse = [], []
+    for b in range(len(q)):
+        ob, lb = [], []
+        for h in range(len(q[b])):
+            oh, lh = _head_forward(q[b][h], k[b][h], v[b][h], scale)
+            ob.append(oh)
+            lb.append(lh)
+        o.append(ob)
+        lse.append(lb)
+    return o, lse
+
+
+def backward(q, k, v, do, scale):
+    """Returns ``(dq, dk, dv)`` as nested lists for L = sum(O * dO)."""
+    dq, dk, dv = [], [], []
+    for b in range(len(q)):
+        qb, kb, vb = [], [], []
+        for h in range(len(q[b])):
+            a, c, e = _head_backward(q[b][h], k[b][h], v[b][h], do[b][h], scale)
+            qb.append(a)
+            kb.append(c)
+            vb.append(e)
+        dq.append(qb)
+        dk.append(kb)
+        dv.append(vb)
+    return dq, dk, dv
