@@ -1,0 +1,274 @@
+"""Benchmark: causal attention forward + backward on one MI355X.
+
+One step = the whole hot path on one batch: gptattn_fwd (attn_fwd kernel),
+then the backward as its two launches gptattn_bwd_dq (attn_bwd_dq) and
+gptattn_bwd_dkdv (attn_bwd_dkdv), on the GPT-2 124M attention shape
+(B=12, H=12, T=1024, D=64, bf16) with inputs resident in HBM.
+
+Throughput counts algorithmic work only: 6 * D * T * (T + 1) flops per
+head-problem (QK^T and PV forward; dV, dP, dQ, dK backward over the causal
+triangle including the diagonal).  Score recomputation in the backward is
+implementation work and is not counted.
+
+Prints one JSON line.  Per-kernel durations come from HIP events recorded on
+the launch stream around every launch of the timed steps.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "causal attn fwd+bwd TFLOP/s at GPT-2 124M shape; % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gpt2_124m.json")
+KERNEL_SOURCES = ["attn_bf16.hip", "attn_common.h"]
+
+
+def unit_flops(N, T, D):
+    """Flops of one causal product (T(T+1)/2 pairs x D multiply-adds x 2)."""
+    return N * D * T * (T + 1)
+
+
+def kernel_table(N, T, D):
+    """Algorithmic flops and bytes per launch of each kernel (bf16)."""
+    u = unit_flops(N, T, D)
+    t = N * T * D * 2      # one bf16 [B,H,T,D] tensor
+    r = N * T * 4          # one float32 [B,H,T] vector
+    return {
+        # QK^T and PV; reads Q, K, V, writes O and lse
+        "attn_fwd": {"flops": 2 * u, "bytes": 4 * t + r},
+        # the dQ product; reads Q, K, V, O, dO, lse, writes dQ and the row term
+        "attn_bwd_dq": {"flops": 1 * u, "bytes": 6 * t + 2 * r},
+        # dP, dV and dK products; reads Q, K, V, dO, lse, row term, writes dK, dV
+        "attn_bwd_dkdv": {"flops": 3 * u, "bytes": 6 * t + 2 * r},
+    }
+
+
+def source_sha():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "causal_self_attention_gptattn_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed counter profile, or None if
+    there is none or the kernel sources changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha") != source_sha():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return int(k["fetch_bytes"] + k["write_bytes"])
+
+
+def cpu_baseline(inp, budget_s):
+    """Time the float64 oracle on a bounded sample of whole heads."""
+    import numpy as np
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import attention as A
+
+    q, k, v, do = (inp[n].float().numpy() for n in ("q", "k", "v", "do"))
+    B, H, T, D = q.shape
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    heads = [(b, h) for b in range(B) for h in range(H)]
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=cores):
+        used = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        while True:
+            b, h = heads[done % len(heads)]
+            A.forward_head(q[b, h], k[b, h], v[b, h], inp["scale"])
+            A.backward_head(q[b, h], k[b, h], v[b, h], do[b, h], inp["scale"])
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+    dt = time.perf_counter() - t0
+    flops = 6 * done * D * T * (T + 1)
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(used),
+        "kind": "oracle",
+        "sample": "%d head-problems (cycling over the %d heads of B=%d, H=%d, T=%d, D=%d), "
+                  "float64 numpy oracle forward + backward, %.1f s, %s"
+                  % (done, B * H, B, H, T, D, dt, platform.processor() or platform.machine()),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gpt2_124m")
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--cold-steps", type=int, default=20,
+                    help="extra steps timed with the caches flushed before each one")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import causal_self_attention_gptattn_amd as G
+    from causal_self_attention_gptattn_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = W.WORKLOADS[args.workload]
+    if w.dtype != "bf16":
+        raise SystemExit("bench.py times the bf16 path")
+    print("bench: generating %s inputs" % w.name, file=sys.stderr, flush=True)
+    inp = W.workload_inputs(w.name, seed=0)
+    B, H, T, D, N = w.B, w.H, w.T, w.D, w.N
+    sc = inp["scale"]
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    ws_bytes = G.workspace_bytes(B, H, T, D)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    lib = G.library()
+    P = lambda t: t.data_ptr()  # noqa: E731
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+
+    def fwd():
+        return lib.gptattn_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, T, D, sc, sp)
+
+    def bdq():
+        return lib.gptattn_bwd_dq(P(q), P(k), P(v), P(o), P(do), P(lse), P(dq), B, H, T, D, sc,
+                                  P(ws), ws_bytes, sp)
+
+    def bdkdv():
+        return lib.gptattn_bwd_dkdv(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, T, D,
+                                    sc, P(ws), ws_bytes, sp)
+
+    launches = [("attn_fwd", fwd), ("attn_bwd_dq", bdq), ("attn_bwd_dkdv", bdkdv)]
+
+    def step(events=None):
+        for i, (name, fn) in enumerate(launches):
+            if events is not None:
+                events[i].record(stream)
+            rc = fn()
+            if rc != 0:
+                raise RuntimeError("%s: %s" % (name, G.status_string(rc)))
+        if events is not None:
+            events[len(launches)].record(stream)
+
+    print("bench: warmup %d steps" % args.warmup, file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+           for _ in range(args.steps)]
+    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+
+    per_kernel_ms = {name: 0.0 for name, _ in launches}
+    for e in evs:
+        for i, (name, _) in enumerate(launches):
+            per_kernel_ms[name] += e[i].elapsed_time(e[i + 1])
+    per_kernel_ms = {k_: t / args.steps for k_, t in per_kernel_ms.items()}
+
+    # Cold-cache steps: overwrite a 1 GiB buffer before each (outside events).
+    cold_ms = None
+    if args.cold_steps > 0:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+               for _ in range(args.cold_steps)]
+        for e in cev:
+            flush.fill_(1)
+            e[0].record(stream)
+            step()
+            e[1].record(stream)
+        torch.cuda.synchronize(dev)
+        cold_ms = sum(a.elapsed_time(b) for a, b in cev) / args.cold_steps
+        del flush
+
+    flops = 6 * N * D * T * (T + 1)
+    ms = wall * 1e3 / args.steps
+    value = flops / (wall / args.steps) / 1e12
+    table = kernel_table(N, T, D)
+    dom = max(per_kernel_ms, key=per_kernel_ms.get)
+    dom_s = per_kernel_ms[dom] * 1e-3
+    achieved = table[dom]["flops"] / dom_s / 1e12
+    kernels = {}
+    for name, t_ms in per_kernel_ms.items():
+        kernels[name] = {
+            "ms": round(t_ms, 5),
+            "alg_tflops": round(table[name]["flops"] / (t_ms * 1e-3) / 1e12, 2),
+            "alg_gbs": round(table[name]["bytes"] / (t_ms * 1e-3) / 1e9, 1),
+        }
+    traffic = measured_traffic(dom)
+
+    base = None
+    if args.cpu_budget > 0:
+        print("bench: oracle CPU baseline (%.0f s budget)" % args.cpu_budget,
+              file=sys.stderr, flush=True)
+        base = cpu_baseline(inp, args.cpu_budget)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": B, "H": H, "T": T, "D": D, "causal": True,
+                   "scale": sc, "alg_gflop_per_step": round(flops / 1e9, 3)},
+        "pct_of_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "kernels": kernels,
+        "cold_cache_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
+        "roofline": {
+            "kernel": dom,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": base,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,1 +1,236 @@
-"""MI355X-native causal self-attention (placeholder; binding follows)."""
+"""Causal scaled dot-product self-attention for AMD MI355X (gfx950).
+
+Thin Python binding over ``libgptattn.so`` (C ABI declared in
+``include/gptattn.h``).  This module only marshals arguments: it checks
+tensor shapes/dtypes/devices, allocates output tensors with PyTorch (device
+memory is PyTorch's job here) and passes raw device pointers plus the current
+HIP stream.  Every arithmetic step runs in the library's HIP kernels; there
+is no fallback.  If the library is missing, every call raises.
+
+Operation (lecture description "Let's build GPT: from scratch, in code,
+spelled out": "version 3: adding softmax", "version 4: self-attention",
+note 6 and the corrections at 00:57:00 and 01:20:05; heads as a batch
+dimension per EX1):
+
+    O   = softmax(scale * Q K^T, keys j <= i only) V
+    lse = log sum_{j <= i} exp(scale * q_i . k_j)
+
+Tensors are ``[B, H, T, D]`` contiguous, bfloat16 (D in {64, 128}) or
+float32 (D in {16, 32, 64}); ``lse`` is ``[B, H, T]`` float32.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "fwd", "bwd", "bwd_dq", "bwd_dkdv", "attention", "GPTAttnFunction", "workspace_bytes",
+    "status_string", "version", "library", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptattn.so")
+
+_LIB = None
+_p = ctypes.c_void_p
+_i = ctypes.c_int
+_f = ctypes.c_float
+_sz = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/gptattn.h
+SIGNATURES = {
+    "gptattn_fwd": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p]),
+    "gptattn_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p, _sz, _p]),
+    "gptattn_bwd_dq": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p, _sz, _p]),
+    "gptattn_bwd_dkdv": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p, _sz, _p]),
+    "gptattn_fwd_f32": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p]),
+    "gptattn_bwd_dq_f32": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p, _sz, _p]),
+    "gptattn_bwd_dkdv_f32": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p, _sz,
+                                  _p]),
+    "gptattn_bwd_f32": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p, _sz, _p]),
+    "gptattn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "gptattn_status_string": (ctypes.c_char_p, [_i]),
+    "gptattn_version": (_i, []),
+}
+
+
+def library():
+    """Load ``libgptattn.so`` (once) and return the ctypes handle."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libgptattn.so is not built (expected at %s); build it with "
+                "`python -m causal_self_attention_gptattn_amd._build`" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = lib
+    return _LIB
+
+
+def status_string(rc):
+    return library().gptattn_status_string(int(rc)).decode()
+
+
+def version():
+    return library().gptattn_version()
+
+
+def workspace_bytes(B, H, T, D, is_f32=False):
+    return library().gptattn_bwd_workspace_bytes(B, H, T, D, 1 if is_f32 else 0)
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise RuntimeError("%s failed: %s" % (what, status_string(rc)))
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _validate(ref, *others):
+    if ref.dim() != 4:
+        raise ValueError("expected [B, H, T, D] tensors, got shape %s" % (tuple(ref.shape),))
+    if not ref.is_cuda:
+        raise ValueError("tensors must live on a GPU")
+    if ref.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("dtype must be bfloat16 or float32, got %s" % ref.dtype)
+    for t in (ref,) + others:
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q, k, v (and o, dO) must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous [B, H, T, D]")
+
+
+def _scale(scale, D):
+    return float(1.0 / math.sqrt(D)) if scale is None else float(scale)
+
+
+def fwd(q, k, v, scale=None, out=None, lse=None):
+    """Forward pass; returns ``(o, lse)``.
+
+    ``out``/``lse`` may be passed to reuse buffers (they are overwritten).
+    """
+    _validate(q, k, v)
+    B, H, T, D = q.shape
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+    _validate(q, out)
+    if lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    lib = library()
+    fn = lib.gptattn_fwd if q.dtype == torch.bfloat16 else lib.gptattn_fwd_f32
+    with torch.cuda.device(q.device):
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, T, D,
+                _scale(scale, D), _stream(q.device))
+    _check(rc, "gptattn_fwd")
+    return out, lse
+
+
+def bwd(q, k, v, o, do, lse, scale=None, dq=None, dk=None, dv=None, workspace=None):
+    """Backward pass for dL/dO = ``do``; returns ``(dq, dk, dv)``."""
+    _validate(q, k, v, o, do)
+    B, H, T, D = q.shape
+    if lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _validate(q, dq, dk, dv)
+    is_f32 = q.dtype == torch.float32
+    need = workspace_bytes(B, H, T, D, is_f32)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    lib = library()
+    fn = lib.gptattn_bwd_f32 if is_f32 else lib.gptattn_bwd
+    with torch.cuda.device(q.device):
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), _ptr(dk),
+                _ptr(dv), B, H, T, D, _scale(scale, D), _ptr(workspace),
+                workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(rc, "gptattn_bwd")
+    return dq, dk, dv
+
+
+def _rows_ok(t, q):
+    B, H, T, _ = q.shape
+    if t.shape != (B, H, T) or t.dtype != torch.float32 or not t.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+
+
+def _ws(workspace, q):
+    B, H, T, D = q.shape
+    need = workspace_bytes(B, H, T, D, q.dtype == torch.float32)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def bwd_dq(q, k, v, o, do, lse, scale=None, dq=None, workspace=None):
+    """First backward launch: dq, plus the row term stored in ``workspace``.
+
+    Returns ``(dq, workspace)``; pass that workspace to :func:`bwd_dkdv`.
+    """
+    _validate(q, k, v, o, do)
+    _rows_ok(lse, q)
+    B, H, T, D = q.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    _validate(q, dq)
+    workspace, nbytes = _ws(workspace, q)
+    lib = library()
+    fn = lib.gptattn_bwd_dq_f32 if q.dtype == torch.float32 else lib.gptattn_bwd_dq
+    with torch.cuda.device(q.device):
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _ptr(dq), B, H, T, D,
+                _scale(scale, D), _ptr(workspace), nbytes, _stream(q.device))
+    _check(rc, "gptattn_bwd_dq")
+    return dq, workspace
+
+
+def bwd_dkdv(q, k, v, do, lse, workspace, scale=None, dk=None, dv=None):
+    """Second backward launch: dk, dv from the row term in ``workspace``."""
+    _validate(q, k, v, do)
+    _rows_ok(lse, q)
+    B, H, T, D = q.shape
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _validate(q, dk, dv)
+    lib = library()
+    fn = lib.gptattn_bwd_dkdv_f32 if q.dtype == torch.float32 else lib.gptattn_bwd_dkdv
+    with torch.cuda.device(q.device):
+        rc = fn(_ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse), _ptr(dk), _ptr(dv), B, H, T, D,
+                _scale(scale, D), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                _stream(q.device))
+    _check(rc, "gptattn_bwd_dkdv")
+    return dk, dv
+
+
+class GPTAttnFunction(torch.autograd.Function):
+    """Autograd wrapper: saves (q, k, v, o, lse) and calls :func:`bwd`."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, scale=None):
+        o, lse = fwd(q, k, v, scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.scale = scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, do.contiguous(), lse, ctx.scale)
+        return dq, dk, dv, None
+
+
+def attention(q, k, v, scale=None):
+    """Differentiable causal self-attention over ``[B, H, T, D]`` tensors."""
+    return GPTAttnFunction.apply(q, k, v, scale)

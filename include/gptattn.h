@@ -1,0 +1,167 @@
+/*
+ * gptattn -- batched multi-head causal scaled dot-product self-attention,
+ * forward and backward, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (lecture description "Let's build GPT: from scratch, in
+ * code, spelled out", chapters "version 3: adding softmax" and "THE CRUX OF
+ * THE VIDEO: version 4: self-attention", note 6 on scaled attention and the
+ * corrections at 00:57:00 and 01:20:05; chapter "batched multi-headed
+ * self-attention" and exercise EX1 for heads as a batch dimension):
+ *
+ *   for every batch element b and head h (independent problems):
+ *     S[i][j]  = scale * sum_d Q[i][d] K[j][d]      for keys j <= i
+ *     P[i][.]  = softmax over the visible keys j <= i (future keys get 0)
+ *     O[i][d]  = sum_j P[i][j] V[j][d]
+ *     lse[i]   = log(sum_{j<=i} exp(S[i][j]))       natural log
+ *
+ * The backward pass returns the gradients of a scalar loss L given
+ * dO = dL/dO:  dV = P^T dO,  dP = dO V^T,
+ *   dS[i][j] = P[i][j] (dP[i][j] - sum_k P[i][k] dP[i][k]),
+ *   dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ * Layout: every tensor is a dense row-major [B][H][T][D] array (D fastest,
+ * heads as a batch dimension); lse is [B][H][T] float32.  T may be any
+ * positive length.  `scale` is passed explicitly (1/sqrt(D) for standard
+ * attention).
+ *
+ * Precision: the *_bf16 entry points (named without suffix) read and write
+ * bfloat16 tensors, multiply on the matrix cores in bf16 with float32
+ * accumulation, keep softmax statistics in float32, and round P and dS to
+ * bf16 before the products that consume them.  The *_f32 entry points do
+ * every step in float32.
+ *
+ * Ownership and execution: the caller owns every buffer (device memory).
+ * The library allocates nothing, frees nothing, never synchronises and never
+ * changes the current device; all work is enqueued on `stream`, a
+ * hipStream_t passed as void* (NULL = the default stream), and completes
+ * asynchronously.  Outputs are fully overwritten, never accumulated.  Inputs
+ * are read only.  Outputs may not overlap the inputs or each other.
+ *
+ * Errors: every entry point returns 0 (GPTATTN_SUCCESS) or a status code.
+ * Arguments are validated before any HIP call, so a call that returns
+ * INVALID_VALUE, NOT_SUPPORTED or WORKSPACE has enqueued nothing.
+ * GPTATTN_ERROR_LAUNCH reports a failed kernel launch.  Faults inside a
+ * kernel surface at the caller's next synchronisation.  Nothing aborts and
+ * no C++ exception crosses this interface.
+ *
+ * Thread safety: stateless and reentrant; concurrent calls on different
+ * streams are safe provided their buffers do not overlap.
+ */
+#ifndef GPTATTN_H
+#define GPTATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gptattn_status {
+  GPTATTN_SUCCESS = 0,
+  /* null or misaligned pointer, B/H/T/D < 1, scale not finite or <= 0,
+     overlapping output buffers, or sizes that overflow 64-bit indexing */
+  GPTATTN_ERROR_INVALID_VALUE = 1,
+  /* head size D outside the compiled set (bf16: 64, 128; f32: 16, 32, 64) */
+  GPTATTN_ERROR_NOT_SUPPORTED = 2,
+  /* backward workspace null or smaller than gptattn_bwd_workspace_bytes() */
+  GPTATTN_ERROR_WORKSPACE = 3,
+  /* a kernel launch failed (hipLaunchKernel returned an error) */
+  GPTATTN_ERROR_LAUNCH = 4
+};
+
+/* Required alignment, in bytes, of every tensor pointer. */
+#define GPTATTN_ALIGNMENT 16
+
+/*
+ * Forward pass, bfloat16 tensors.
+ *   q, k, v : [B][H][T][D] bf16, read only.
+ *   o       : [B][H][T][D] bf16, written: softmax(scale Q K^T + causal) V.
+ *   lse     : [B][H][T] float32, written: natural-log row normaliser of the
+ *             scaled, masked scores (kept for the backward pass).
+ *   D must be 64 or 128.
+ */
+int gptattn_fwd(const void* q, const void* k, const void* v, void* o,
+                float* lse, int B, int H, int T, int D, float scale,
+                void* stream);
+
+/*
+ * Backward pass, bfloat16 tensors.
+ *   q, k, v, o, dO : [B][H][T][D] bf16, read only (o and lse as written by
+ *                    gptattn_fwd for the same q, k, v, scale).
+ *   lse            : [B][H][T] float32, read only.
+ *   dq, dk, dv     : [B][H][T][D] bf16, written.
+ *   workspace      : device scratch of at least
+ *                    gptattn_bwd_workspace_bytes(B, H, T, D, 0) bytes; its
+ *                    contents on entry are ignored and on return undefined.
+ *   D must be 64 or 128.
+ * The loss gradient dO is taken as given (dL/dO); the row term
+ * sum_k P[i][k] dP[i][k] is formed as sum_d dO[i][d] O[i][d].
+ */
+int gptattn_bwd(const void* q, const void* k, const void* v, const void* o,
+                const void* dO, const float* lse, void* dq, void* dk,
+                void* dv, int B, int H, int T, int D, float scale,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The backward pass as its two launches, for callers that schedule them
+ * separately (for example to overlap dK/dV with other work, or to time
+ * each kernel).  gptattn_bwd == gptattn_bwd_dq followed, on the same stream,
+ * by gptattn_bwd_dkdv with the same workspace.
+ *
+ * gptattn_bwd_dq writes dq and stores the row term sum_d dO O (B*H*T
+ * float32) in `workspace`.  gptattn_bwd_dkdv reads that row term from
+ * `workspace` (which must hold the values gptattn_bwd_dq stored for the
+ * same inputs, on the same stream or after synchronising) and writes dk, dv.
+ * Arguments as for gptattn_bwd.
+ */
+int gptattn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                   const void* dO, const float* lse, void* dq, int B, int H,
+                   int T, int D, float scale, void* workspace,
+                   size_t workspace_bytes, void* stream);
+int gptattn_bwd_dkdv(const void* q, const void* k, const void* v,
+                     const void* dO, const float* lse, void* dk, void* dv,
+                     int B, int H, int T, int D, float scale,
+                     const void* workspace, size_t workspace_bytes,
+                     void* stream);
+
+/* Forward pass, float32 tensors; same contract, D in {16, 32, 64}. */
+int gptattn_fwd_f32(const float* q, const float* k, const float* v,
+                    float* o, float* lse, int B, int H, int T, int D,
+                    float scale, void* stream);
+
+/* Backward pass, float32 tensors; same contract, D in {16, 32, 64}. */
+int gptattn_bwd_f32(const float* q, const float* k, const float* v,
+                    const float* o, const float* dO, const float* lse,
+                    float* dq, float* dk, float* dv, int B, int H, int T,
+                    int D, float scale, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* The two backward launches, float32 tensors (see gptattn_bwd_dq). */
+int gptattn_bwd_dq_f32(const float* q, const float* k, const float* v,
+                       const float* o, const float* dO, const float* lse,
+                       float* dq, int B, int H, int T, int D, float scale,
+                       void* workspace, size_t workspace_bytes, void* stream);
+int gptattn_bwd_dkdv_f32(const float* q, const float* k, const float* v,
+                         const float* dO, const float* lse, float* dk,
+                         float* dv, int B, int H, int T, int D, float scale,
+                         const void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
+ * Bytes of device workspace gptattn_bwd / gptattn_bwd_f32 need for the given
+ * shape (is_f32 selects the float32 entry point); 0 if the shape is invalid.
+ * Holds the float32 row term sum_d dO O, B*H*T values.
+ */
+size_t gptattn_bwd_workspace_bytes(int B, int H, int T, int D, int is_f32);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* gptattn_status_string(int status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int gptattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTATTN_H */

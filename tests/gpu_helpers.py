@@ -1,0 +1,101 @@
+"""Shared helpers for the GPU tests: run the HIP path through the C ABI and
+compare it with the float64 oracle on the same seeded inputs."""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import causal_self_attention_gptattn_amd as G
+from oracle import attention as A
+
+# Tolerances, per element |gpu - oracle| <= abs + rel_elem * |oracle|:
+#   bf16: abs 2e-2 on outputs and gradients plus one bf16 unit round-off
+#         (2^-8) of the value itself -- a bf16 result of magnitude >= 8 is
+#         only representable to within 2^-5, so a pure 2e-2 bound would be
+#         below the storage format's own resolution there.  On top of that a
+#         relative Frobenius bound of 1e-2 per tensor pins small gradients
+#         (2e-2 absolute alone would accept an all-zero dQ).  lse (float32
+#         in both precisions) 1e-3 absolute.
+#   f32:  1e-5 absolute everywhere.
+TOL = {
+    "bf16": {"abs": 2e-2, "rel_elem": 2.0 ** -8, "rel_fro": 1e-2, "lse": 1e-3},
+    "f32": {"abs": 1e-5, "rel_elem": 0.0, "rel_fro": 1e-5, "lse": 1e-5},
+}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    return torch.device("cuda:0")
+
+
+def to64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def run_gpu(inp, dev):
+    """Forward + backward through the library; returns float64 numpy dict."""
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = G.fwd(q, k, v, inp["scale"])
+    dq, dk, dv = G.bwd(q, k, v, o, do, lse, inp["scale"])
+    torch.cuda.synchronize(dev)
+    return {"o": to64(o), "lse": to64(lse), "dq": to64(dq), "dk": to64(dk), "dv": to64(dv)}
+
+
+def run_oracle(inp, heads=None):
+    q, k, v, do = (inp[n].to(torch.float64).numpy() for n in ("q", "k", "v", "do"))
+    o, lse = A.forward(q, k, v, inp["scale"], heads=heads)
+    dq, dk, dv = A.backward(q, k, v, do, inp["scale"], heads=heads)
+    return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+
+
+def compare(got, ref, dtype, heads=None, label=""):
+    """Assert parity on all heads or on the listed (b, h) heads."""
+    tol = TOL[dtype]
+    report = {}
+    for name in ("o", "lse", "dq", "dk", "dv"):
+        g, r = got[name], ref[name]
+        if heads is not None:
+            g = np.stack([g[b, h] for b, h in heads])
+            r = np.stack([r[b, h] for b, h in heads])
+        assert np.isfinite(g).all(), "%s %s: non-finite GPU output" % (label, name)
+        diff = np.abs(g - r)
+        err = diff.max()
+        rnorm = np.linalg.norm(r)
+        rel = np.linalg.norm(g - r) / rnorm if rnorm > 0 else 0.0
+        report[name] = (err, rel)
+        if name == "lse":
+            assert err <= tol["lse"], "%s lse: max abs err %.3e > %.1e" % (label, err, tol["lse"])
+            continue
+        lim = tol["abs"] + tol["rel_elem"] * np.abs(r)
+        worst = np.unravel_index(np.argmax(diff - lim), diff.shape)
+        assert (diff <= lim).all(), "%s %s: err %.3e at ref %.3e exceeds %.3e" % (
+            label, name, diff[worst], r[worst], lim[worst])
+        if rnorm > 0:
+            assert rel <= tol["rel_fro"], "%s %s: rel Frobenius err %.3e > %.1e" % (
+                label, name, rel, tol["rel_fro"])
+        else:
+            assert err <= tol["abs"]
+    say(label, " ".join("%s=%.2e/%.2e" % (n, e, r) for n, (e, r) in report.items()))
+    return report
+
+
+def sample_heads(B, H, count, seed):
+    rng = np.random.default_rng(1000 + seed)
+    pairs = [(b, h) for b in range(B) for h in range(H)]
+    if count >= len(pairs):
+        return pairs
+    idx = rng.choice(len(pairs), size=count, replace=False)
+    chosen = [pairs[i] for i in sorted(idx)]
+    # always include the first and the last head
+    for p in (pairs[0], pairs[-1]):
+        if p not in chosen:
+            chosen.append(p)
+    return chosen
