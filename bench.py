@@ -122,7 +122,22 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps timed with the caches flushed before each one")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 5 device-to-device copies of MIB MiB (calibrates the "
+                         "HBM byte counters against a copy of known size) and exit")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        import torch
+
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_per_launch": {"read": n, "write": n}, "launches": 5}))
+        return
 
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "

@@ -19,7 +19,8 @@
 //                 softmax (running max m and sum l) stays in registers, the
 //                 row reductions need one cross-half exchange, and the bf16
 //                 probabilities feed O^T += V^T P^T straight from registers.
-//                 K is staged row-major in LDS, V transposed.
+//                 K and V are staged row-major in LDS; V^T is read with
+//                 the gfx950 transpose read (attn_common.h).
 //   attn_bwd_dq   same tiling as attn_fwd.  First forms the row term
 //                 delta_i = sum_d dO_id O_id (written to the workspace for
 //                 attn_bwd_dkdv), then recomputes P^T from lse, dP^T = V dO^T,
@@ -28,8 +29,8 @@
 //                 query tiles from the diagonal to the end with the lane ->
 //                 key layout: S = Q K^T and dP = dO V^T, then
 //                 dV^T += dO^T P and dK^T += Q^T dS with P and dS taken from
-//                 registers.  Q and dO are staged both row-major and
-//                 transposed in LDS.
+//                 registers.  Q and dO are staged row-major in LDS and
+//                 read transposed for the dV/dK products.
 //
 // dQ and dK/dV come from separate kernels, so no result is accumulated with
 // atomics and every output is bitwise reproducible run to run.
@@ -41,32 +42,97 @@ namespace gptattn {
 namespace {
 
 constexpr int kThreads = 256;  // 4 waves
+constexpr float kLazy = 8.0f;  // log2 headroom before the running max is moved
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
 
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
+
+// One 64-key tile for one wave (32 queries, one per lane column c), taken
+// as two 32-key halves with one online-softmax step each, which keeps only
+// half a tile of scores live.  MASK is set only for tiles that straddle the
+// diagonal (or the end of the sequence).
+template <int D, bool MASK>
+__device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf,
+                                         f32x16* ot, float& m, float& l, int k0, int qi, int c,
+                                         int g, int tro, float sl2) {
+  constexpr int LD = D + 8, DS = D / 16, DE = D / 32;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    // S^T = K Q^T for 32 keys: rows = keys, columns = this wave's queries
+    f32x16 st = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 8 * g), qf[0], zero16());
+#pragma unroll
+    for (int s = 1; s < DS; ++s)
+      st = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 16 * s + 8 * g), qf[s], st);
+    if (MASK) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = k0 + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
+        if (key > qi) st[r] = -INFINITY;
+      }
+    }
+    float mx = st[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
+    mx = fmaxf(mx, wave_xor32(mx)) * sl2;
+    // Lazy rescaling: the reference max m only moves when some row of the
+    // wave sees a score more than 2^kLazy above it.  Until then the
+    // probabilities exp2(s - m) stay below 2^kLazy, which bf16 and the
+    // float32 accumulators hold exactly as well; O and l share the same
+    // reference, so the final O / l is unchanged.
+    if (__any(mx > m + kLazy)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      m = mnew;
+      l *= alpha;
+#pragma unroll
+      for (int e = 0; e < DE; ++e) ot[e] *= alpha;
+    }
+    const float nm = -m;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float p[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[8 * t + j], sl2, nm));
+        l += p[j];
+      }
+      pf[t] = pack_bf16x8(p);
+    }
+    // O^T += V^T P^T, V^T read transposed from the row-major V tile
+#pragma unroll
+    for (int e = 0; e < DE; ++e)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        ot[e] = mfma32x32x16(ld_frag_tr(vb + (32 * a + 16 * t) * LD + 32 * e + tro, LD), pf[t],
+                             ot[e]);
+  }
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_fwd(
+__global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
     float* __restrict__ LSE, int N, int T, float sl2, int nqb) {
   constexpr int BM = 128, BN = 64;
-  constexpr int KLD = D + 8;    // row-major K tile, padded
-  constexpr int VLD = BN + 4;   // transposed V tile, padded
+  constexpr int LD = D + 8;     // padded row stride of the LDS tiles
   constexpr int DS = D / 16;    // k-steps of the score product
   constexpr int DE = D / 32;    // 32-row output tiles over the head dim
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2][D * VLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * LD];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
+  const int tro = tr_rowoff(lane) * LD + tr_coloff(lane);
   const int bid = blockIdx.x;
   const int qb = nqb - 1 - bid / N;  // longest query blocks first
   const int n = bid % N;
-  const size_t head = (size_t)n * T * D;
+  const uint16_t* Kh = K + (size_t)n * T * D;
+  const uint16_t* Vh = V + (size_t)n * T * D;
   const int q0 = qb * BM;
   const int q0w = q0 + 32 * w;
   const int qi = q0w + c;
@@ -75,7 +141,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_fwd(
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
     if (qi < T) {
-      qf[s] = ld_frag16(Q + head + (size_t)qi * D + 16 * s + 8 * g);
+      qf[s] = ld_frag16(Q + ((size_t)n * T + qi) * D + 16 * s + 8 * g);
     } else {
       qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
@@ -85,11 +151,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_fwd(
   const int nkt = (kend - 1) / BN + 1;
   const int wnkt = q0w < T ? (min(q0w + 32, T) - 1) / BN + 1 : 0;
 
-  TileStage<BN, D, kThreads> ks, vs;
-  ks.load(K + head, T, tid);
-  vs.load(V + head, T, tid);
-  ks.store_rowmajor(Ks[0], KLD, tid);
-  vs.store_transposed(Vt[0], VLD, tid);
+  RowStage<BN, D, kThreads> ks, vs;
+  ks.init(tid, LD);
+  vs.init(tid, LD);
+  ks.load(Kh, T);
+  vs.load(Vh, T);
+  ks.store(Ks[0], LD);
+  vs.store(Vs[0], LD);
   __syncthreads();
 
   f32x16 ot[DE];
@@ -102,68 +170,20 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_fwd(
     const bool more = kt + 1 < nkt;
     if (more) {
       const int k1 = (kt + 1) * BN;
-      ks.load(K + head + (size_t)k1 * D, T - k1, tid);
-      vs.load(V + head + (size_t)k1 * D, T - k1, tid);
+      ks.load(Kh + (size_t)k1 * D, T - k1);
+      vs.load(Vh + (size_t)k1 * D, T - k1);
     }
     if (kt < wnkt) {
       const int k0 = kt * BN;
-      const uint16_t* kb = Ks[buf];
-      const uint16_t* vb = Vt[buf];
-      f32x16 st[2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        st[a] = zero16();
-#pragma unroll
-        for (int s = 0; s < DS; ++s)
-          st[a] = mfma32x32x16(ld_frag16(kb + (32 * a + c) * KLD + 16 * s + 8 * g), qf[s], st[a]);
-      }
-      if (k0 + BN - 1 > q0w) {  // tile straddles the diagonal (or the end)
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
-            if (key > qi) st[a][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, st[a][r]);
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float mnew = fmaxf(m, mx * sl2);
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      m = mnew;
-      float ps = 0.0f;
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float p[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[a][8 * t + j], sl2, -mnew));
-            ps += p[j];
-          }
-          pf[a][t] = pack_bf16x8(p);
-        }
-      l = l * alpha + ps;
-#pragma unroll
-      for (int e = 0; e < DE; ++e) {
-        ot[e] *= alpha;
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            ot[e] = mfma32x32x16(ld_frag_split(vb + (32 * e + c) * VLD + 32 * a + 16 * t + 4 * g),
-                                 pf[a][t], ot[e]);
+      if (k0 + BN - 1 > q0w) {
+        fwd_tile<D, true>(Ks[buf], Vs[buf], qf, ot, m, l, k0, qi, c, g, tro, sl2);
+      } else {
+        fwd_tile<D, false>(Ks[buf], Vs[buf], qf, ot, m, l, k0, qi, c, g, tro, sl2);
       }
     }
     if (more) {
-      ks.store_rowmajor(Ks[buf ^ 1], KLD, tid);
-      vs.store_transposed(Vt[buf ^ 1], VLD, tid);
+      ks.store(Ks[buf ^ 1], LD);
+      vs.store(Vs[buf ^ 1], LD);
     }
     __syncthreads();
   }
@@ -171,7 +191,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_fwd(
   const float lt = l + wave_xor32(l);
   if (qi < T) {
     const float inv = 1.0f / lt;
-    uint16_t* orow = O + head + (size_t)qi * D;
+    uint16_t* orow = O + ((size_t)n * T + qi) * D;
 #pragma unroll
     for (int e = 0; e < DE; ++e)
 #pragma unroll
@@ -187,29 +207,74 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_fwd(
 // ---------------------------------------------------------------------------
 // Backward, part 1: row term delta and dQ (lane -> query layout)
 // ---------------------------------------------------------------------------
+
+// One 64-key tile for one wave of the dQ kernel, taken as two 32-key
+// halves.  nd holds -delta of this lane's query in all 16 slots; it seeds
+// the dP^T accumulator so that the product directly yields dP^T - delta.
+template <int D, bool MASK>
+__device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf,
+                                        const bf16x8* df, const f32x16& nd, f32x16* acc, int k0,
+                                        int qi, int c, int g, int tro, float sl2, float nl) {
+  constexpr int LD = D + 8, DS = D / 16, DE = D / 32;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    // S^T = K Q^T and dP^T - delta = V dO^T - delta: rows = keys, columns = queries
+    f32x16 st = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 8 * g), qf[0], zero16());
+    f32x16 dp = mfma32x32x16(ld_frag16(vb + (32 * a + c) * LD + 8 * g), df[0], nd);
+#pragma unroll
+    for (int s = 1; s < DS; ++s) {
+      st = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 16 * s + 8 * g), qf[s], st);
+      dp = mfma32x32x16(ld_frag16(vb + (32 * a + c) * LD + 16 * s + 8 * g), df[s], dp);
+    }
+    bf16x8 sf[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float ds[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 8 * t + j;
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sl2, nl));
+        if (MASK) {
+          const int key = k0 + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (key > qi) p = 0.0f;
+        }
+        ds[j] = p * dp[r];
+      }
+      sf[t] = pack_bf16x8(ds);
+    }
+    // dQ^T += K^T dS^T, K^T read transposed from the row-major K tile
+#pragma unroll
+    for (int e = 0; e < DE; ++e)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        acc[e] = mfma32x32x16(ld_frag_tr(kb + (32 * a + 16 * t) * LD + 32 * e + tro, LD), sf[t],
+                              acc[e]);
+  }
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dq(
+__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void attn_bwd_dq(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
     uint16_t* __restrict__ dQ, float* __restrict__ Delta, int N, int T,
     float sl2, float scale, int nqb) {
   constexpr int BM = 128, BN = 64;
-  constexpr int KLD = D + 8;
-  constexpr int TLD = BN + 4;
+  constexpr int LD = D + 8;
   constexpr int DS = D / 16;
   constexpr int DE = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * KLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[2][D * TLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * LD];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
+  const int tro = tr_rowoff(lane) * LD + tr_coloff(lane);
   const int bid = blockIdx.x;
   const int qb = nqb - 1 - bid / N;
   const int n = bid % N;
-  const size_t head = (size_t)n * T * D;
+  const uint16_t* Kh = K + (size_t)n * T * D;
+  const uint16_t* Vh = V + (size_t)n * T * D;
   const int q0 = qb * BM;
   const int q0w = q0 + 32 * w;
   const int qi = q0w + c;
@@ -219,7 +284,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dq(
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
     if (qi < T) {
-      const size_t off = head + (size_t)qi * D + 16 * s + 8 * g;
+      const size_t off = ((size_t)n * T + qi) * D + 16 * s + 8 * g;
       qf[s] = ld_frag16(Q + off);
       const u32x4 dou = *reinterpret_cast<const u32x4*>(dO + off);
       const u32x4 ou = *reinterpret_cast<const u32x4*>(O + off);
@@ -233,19 +298,23 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dq(
     }
   }
   const float delta = dpart + wave_xor32(dpart);
-  const float lse2 = qi < T ? LSE[(size_t)n * T + qi] * kLog2e : 0.0f;
+  const float nl = qi < T ? -LSE[(size_t)n * T + qi] * kLog2e : 0.0f;
   if (qi < T && g == 0) Delta[(size_t)n * T + qi] = delta;
+  f32x16 nd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) nd[r] = -delta;
 
   const int kend = min(q0 + BM, T);
   const int nkt = (kend - 1) / BN + 1;
   const int wnkt = q0w < T ? (min(q0w + 32, T) - 1) / BN + 1 : 0;
 
-  TileStage<BN, D, kThreads> ks, vs;
-  ks.load(K + head, T, tid);
-  vs.load(V + head, T, tid);
-  ks.store_rowmajor(Ks[0], KLD, tid);
-  ks.store_transposed(Kt[0], TLD, tid);
-  vs.store_rowmajor(Vs[0], KLD, tid);
+  RowStage<BN, D, kThreads> ks, vs;
+  ks.init(tid, LD);
+  vs.init(tid, LD);
+  ks.load(Kh, T);
+  vs.load(Vh, T);
+  ks.store(Ks[0], LD);
+  vs.store(Vs[0], LD);
   __syncthreads();
 
   f32x16 acc[DE];
@@ -257,63 +326,26 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dq(
     const bool more = kt + 1 < nkt;
     if (more) {
       const int k1 = (kt + 1) * BN;
-      ks.load(K + head + (size_t)k1 * D, T - k1, tid);
-      vs.load(V + head + (size_t)k1 * D, T - k1, tid);
+      ks.load(Kh + (size_t)k1 * D, T - k1);
+      vs.load(Vh + (size_t)k1 * D, T - k1);
     }
     if (kt < wnkt) {
       const int k0 = kt * BN;
-      const uint16_t* kb = Ks[buf];
-      const uint16_t* vb = Vs[buf];
-      const uint16_t* tb = Kt[buf];
-      f32x16 st[2], dp[2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        st[a] = zero16();
-        dp[a] = zero16();
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          st[a] = mfma32x32x16(ld_frag16(kb + (32 * a + c) * KLD + 16 * s + 8 * g), qf[s], st[a]);
-          dp[a] = mfma32x32x16(ld_frag16(vb + (32 * a + c) * KLD + 16 * s + 8 * g), df[s], dp[a]);
-        }
+      if (k0 + BN - 1 > q0w) {
+        dq_tile<D, true>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, qi, c, g, tro, sl2, nl);
+      } else {
+        dq_tile<D, false>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, qi, c, g, tro, sl2, nl);
       }
-      const bool diag = k0 + BN - 1 > q0w;
-      bf16x8 sf[2][2];
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float ds[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int r = 8 * t + j;
-            float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[a][r], sl2, -lse2));
-            if (diag) {
-              const int key = k0 + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
-              if (key > qi) p = 0.0f;
-            }
-            ds[j] = p * (dp[a][r] - delta);
-          }
-          sf[a][t] = pack_bf16x8(ds);
-        }
-#pragma unroll
-      for (int e = 0; e < DE; ++e)
-#pragma unroll
-        for (int a = 0; a < 2; ++a)
-#pragma unroll
-          for (int t = 0; t < 2; ++t)
-            acc[e] = mfma32x32x16(ld_frag_split(tb + (32 * e + c) * TLD + 32 * a + 16 * t + 4 * g),
-                                  sf[a][t], acc[e]);
     }
     if (more) {
-      ks.store_rowmajor(Ks[buf ^ 1], KLD, tid);
-      ks.store_transposed(Kt[buf ^ 1], TLD, tid);
-      vs.store_rowmajor(Vs[buf ^ 1], KLD, tid);
+      ks.store(Ks[buf ^ 1], LD);
+      vs.store(Vs[buf ^ 1], LD);
     }
     __syncthreads();
   }
 
   if (qi < T) {
-    uint16_t* row = dQ + head + (size_t)qi * D;
+    uint16_t* row = dQ + ((size_t)n * T + qi) * D;
 #pragma unroll
     for (int e = 0; e < DE; ++e)
 #pragma unroll
@@ -328,6 +360,66 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dq(
 // ---------------------------------------------------------------------------
 // Backward, part 2: dK and dV (lane -> key layout)
 // ---------------------------------------------------------------------------
+
+// One BM-query tile for one wave (32 keys, one per lane column c).  ls/es
+// hold lse * log2(e) and delta of the tile's queries.
+template <int D, int BM, bool MASK>
+__device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db, const float* ls,
+                                          const float* es, const bf16x8* kf, const bf16x8* vf,
+                                          f32x16* dvt, f32x16* dkt, int q0, int kj, int g,
+                                          int c, int tro, float sl2) {
+  constexpr int LD = D + 8, DS = D / 16, DE = D / 32, NH = BM / 32;
+  bf16x8 pf[NH][2], sf[NH][2];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    // per-row statistics of rows 32h + 8u + 4g + i, in result-register order
+    f32x16 nl, nd;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const f32x4 lq = *reinterpret_cast<const f32x4*>(ls + 32 * h + 8 * u + 4 * g);
+      const f32x4 eq = *reinterpret_cast<const f32x4*>(es + 32 * h + 8 * u + 4 * g);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        nl[4 * u + i] = lq[i];
+        nd[4 * u + i] = -eq[i];
+      }
+    }
+    // S = Q K^T and dP - delta = dO V^T - delta: rows = queries, columns = keys
+    f32x16 st = mfma32x32x16(ld_frag16(qb + (32 * h + c) * LD + 8 * g), kf[0], zero16());
+    f32x16 dp = mfma32x32x16(ld_frag16(db + (32 * h + c) * LD + 8 * g), vf[0], nd);
+#pragma unroll
+    for (int s = 1; s < DS; ++s) {
+      st = mfma32x32x16(ld_frag16(qb + (32 * h + c) * LD + 16 * s + 8 * g), kf[s], st);
+      dp = mfma32x32x16(ld_frag16(db + (32 * h + c) * LD + 16 * s + 8 * g), vf[s], dp);
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float p[8], dsv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int r = 8 * t + j;
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sl2, -nl[r]));
+        if (MASK && kj > q0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3)) pv = 0.0f;
+        p[j] = pv;
+        dsv[j] = pv * dp[r];
+      }
+      pf[h][t] = pack_bf16x8(p);
+      sf[h][t] = pack_bf16x8(dsv);
+    }
+  }
+  // dV^T += dO^T P and dK^T += Q^T dS, dO^T and Q^T read transposed
+#pragma unroll
+  for (int e = 0; e < DE; ++e)
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int off = (32 * h + 16 * t) * LD + 32 * e + tro;
+        dvt[e] = mfma32x32x16(ld_frag_tr(db + off, LD), pf[h][t], dvt[e]);
+        dkt[e] = mfma32x32x16(ld_frag_tr(qb + off, LD), sf[h][t], dkt[e]);
+      }
+}
+
 template <int D, int BM>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
@@ -336,25 +428,23 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int T,
     float sl2, float scale, int nkb) {
   constexpr int BN = 128;
-  constexpr int NH = BM / 32;   // 32-query halves per query tile
-  constexpr int RLD = D + 8;    // row-major Q / dO tiles
-  constexpr int TLD = BM + 4;   // transposed Q / dO tiles
+  constexpr int LD = D + 8;     // row-major Q / dO tiles
   constexpr int DS = D / 16;
   constexpr int DE = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BM * RLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Qt[2][D * TLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][BM * RLD];
-  __shared__ __attribute__((aligned(16))) uint16_t Dt[2][D * TLD];
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BM * LD];
+  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][BM * LD];
   __shared__ __attribute__((aligned(16))) float Ls[2][BM];
   __shared__ __attribute__((aligned(16))) float Es[2][BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
+  const int tro = tr_rowoff(lane) * LD + tr_coloff(lane);
   const int bid = blockIdx.x;
   const int kb = bid / N;  // block 0 (the most queries) first
   const int n = bid % N;
-  const size_t head = (size_t)n * T * D;
+  const uint16_t* Qh = Q + (size_t)n * T * D;
+  const uint16_t* Dh = dO + (size_t)n * T * D;
   const size_t rows = (size_t)n * T;
   const int k0 = kb * BN;
   const int k0w = k0 + 32 * w;
@@ -364,7 +454,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
 #pragma unroll
   for (int s = 0; s < DS; ++s) {
     if (kj < T) {
-      const size_t off = head + (size_t)kj * D + 16 * s + 8 * g;
+      const size_t off = (rows + kj) * D + 16 * s + 8 * g;
       kf[s] = ld_frag16(K + off);
       vf[s] = ld_frag16(V + off);
     } else {
@@ -376,12 +466,14 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
   const int qt0 = k0 / BM;
   const int nqt = (T + BM - 1) / BM;
 
-  TileStage<BM, D, kThreads> qs, ds;
+  RowStage<BM, D, kThreads> qs, ds;
+  qs.init(tid, LD);
+  ds.init(tid, LD);
   float lv = 0.0f, ev = 0.0f;
   auto load_tile = [&](int qt) {
     const int q1 = qt * BM;
-    qs.load(Q + head + (size_t)q1 * D, T - q1, tid);
-    ds.load(dO + head + (size_t)q1 * D, T - q1, tid);
+    qs.load(Qh + (size_t)q1 * D, T - q1);
+    ds.load(Dh + (size_t)q1 * D, T - q1);
     if (tid < BM) {
       const int q = q1 + tid;
       lv = q < T ? LSE[rows + q] * kLog2e : INFINITY;
@@ -389,10 +481,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
     }
   };
   auto store_tile = [&](int b) {
-    qs.store_rowmajor(Qs[b], RLD, tid);
-    qs.store_transposed(Qt[b], TLD, tid);
-    ds.store_rowmajor(Ds[b], RLD, tid);
-    ds.store_transposed(Dt[b], TLD, tid);
+    qs.store(Qs[b], LD);
+    ds.store(Ds[b], LD);
     if (tid < BM) {
       Ls[b][tid] = lv;
       Es[b][tid] = ev;
@@ -415,59 +505,21 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
     if (more) load_tile(qt + 1);
     const int q0 = qt * BM;
     if (q0 + BM - 1 >= k0w && k0w < T) {  // some query of the tile sees a key of this wave
-      const uint16_t* qb = Qs[buf];
-      const uint16_t* db = Ds[buf];
-      const uint16_t* qtb = Qt[buf];
-      const uint16_t* dtb = Dt[buf];
-      const bool diag = k0w + 31 > q0;
-      bf16x8 pf[NH][2], sf[NH][2];
-#pragma unroll
-      for (int h = 0; h < NH; ++h) {
-        f32x16 st = zero16(), dp = zero16();
-#pragma unroll
-        for (int s = 0; s < DS; ++s) {
-          st = mfma32x32x16(ld_frag16(qb + (32 * h + c) * RLD + 16 * s + 8 * g), kf[s], st);
-          dp = mfma32x32x16(ld_frag16(db + (32 * h + c) * RLD + 16 * s + 8 * g), vf[s], dp);
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float p[8], dsv[8];
-#pragma unroll
-          for (int u2 = 0; u2 < 2; ++u2) {
-            const int rowb = 32 * h + 16 * t + 8 * u2 + 4 * g;  // 4 consecutive query rows
-            const f32x4 lq = *reinterpret_cast<const f32x4*>(&Ls[buf][rowb]);
-            const f32x4 eq = *reinterpret_cast<const f32x4*>(&Es[buf][rowb]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int r = 8 * t + 4 * u2 + i;
-              float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sl2, -lq[i]));
-              if (diag && kj > q0 + rowb + i) pv = 0.0f;
-              p[4 * u2 + i] = pv;
-              dsv[4 * u2 + i] = pv * (dp[r] - eq[i]);
-            }
-          }
-          pf[h][t] = pack_bf16x8(p);
-          sf[h][t] = pack_bf16x8(dsv);
-        }
+      if (k0w + 31 > q0) {
+        dkdv_tile<D, BM, true>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0, kj, g, c,
+                               tro, sl2);
+      } else {
+        dkdv_tile<D, BM, false>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0, kj, g,
+                                c, tro, sl2);
       }
-#pragma unroll
-      for (int e = 0; e < DE; ++e)
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int off = (32 * e + c) * TLD + 32 * h + 16 * t + 4 * g;
-            dvt[e] = mfma32x32x16(ld_frag_split(dtb + off), pf[h][t], dvt[e]);
-            dkt[e] = mfma32x32x16(ld_frag_split(qtb + off), sf[h][t], dkt[e]);
-          }
     }
     if (more) store_tile(buf ^ 1);
     __syncthreads();
   }
 
   if (kj < T) {
-    uint16_t* krow = dK + head + (size_t)kj * D;
-    uint16_t* vrow = dV + head + (size_t)kj * D;
+    uint16_t* krow = dK + (rows + kj) * D;
+    uint16_t* vrow = dV + (rows + kj) * D;
 #pragma unroll
     for (int e = 0; e < DE; ++e)
 #pragma unroll

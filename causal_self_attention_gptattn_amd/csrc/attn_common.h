@@ -62,78 +62,83 @@ __device__ __forceinline__ bf16x8 ld_frag16(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-// Operand whose eight k-values sit in two runs of four, 8 elements apart
-// (the pattern of a result tile's rows r = 0..7 for one lane half).
-__device__ __forceinline__ bf16x8 ld_frag_split(const uint16_t* p) {
-  u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-  u32x2 hi = *reinterpret_cast<const u32x2*>(p + 8);
-  u32x4 u = {lo[0], lo[1], hi[0], hi[1]};
-  return __builtin_bit_cast(bf16x8, u);
+// ---------------------------------------------------------------------------
+// Transposed operand reads from a row-major LDS tile (gfx950
+// ds_read_b64_tr_b16).  Within each group of 16 lanes, lane i receives
+// element (i % 4) of the 8-byte chunks addressed by lanes 4j + i / 4,
+// j = 0..3.  When the group's lanes address a 4-row x 16-column block
+// (lane L -> row L / 4, columns 4 (L % 4) .. +3), lane i therefore gets
+// column i of the four rows: four consecutive k-values of one MFMA row m.
+//
+// For an A operand X^T[m][k] of v_mfma_f32_32x32x16_bf16 read from a
+// row-major tile X[k][m], lane (c, g) needs k = kb + 4g + {0..3} and
+// kb + 8 + 4g + {0..3} at m = mb + c (the row pattern of a result tile's
+// registers 0..7).  tr_rowoff/tr_coloff give this lane's row and column
+// inside such a 16 x 32 block; ld_frag_tr reads both halves.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int tr_rowoff(int lane) { return 4 * (lane >> 5) + ((lane & 15) >> 2); }
+__device__ __forceinline__ int tr_coloff(int lane) { return 16 * ((lane >> 4) & 1) + 4 * (lane & 3); }
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// p = &X[kb + tr_rowoff][mb + tr_coloff] in LDS, ld = row stride (elements).
+__device__ __forceinline__ bf16x8 ld_frag_tr(const uint16_t* p, int ld) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * ld));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
+  const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+  return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
 
 // ---------------------------------------------------------------------------
 // Global -> LDS staging of a ROWS x D bf16 tile (row-major in HBM, D
-// contiguous).  The tile is cut into 4x4 micro-blocks; thread t of NT owns
-// micro-blocks t, t + NT, ...  Consecutive threads take consecutive column
-// quads of the same row quad, so each wave's global reads cover whole rows.
-// The tile can be written to LDS row-major ([row][col], leading dimension
-// ld) and/or transposed ([col][row]); the transpose is a 4x4 register
-// shuffle of 16-bit values followed by 8-byte LDS writes.
-// Rows at or beyond `valid` read as zero.
+// contiguous) into a row-major LDS tile with leading dimension ld.  Thread t
+// of NT moves 16-byte chunks t, t + NT, ...; eight consecutive threads cover
+// one 128-byte row segment, so each wave's loads and stores are contiguous.
+// Rows at or beyond `valid` read as zero; a full tile takes the unguarded
+// path (one uniform branch per tile).
 // ---------------------------------------------------------------------------
 template <int ROWS, int D, int NT>
-struct TileStage {
-  static constexpr int CQ = D / 4;             // column quads per row
-  static constexpr int MB = ROWS * D / 16;     // micro-blocks in the tile
-  static constexpr int PER = MB / NT;          // micro-blocks per thread
-  static_assert(MB % NT == 0, "tile must split evenly over the threads");
-  u32x2 r[PER][4];
+struct RowStage {
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int PER = ROWS * CPR / NT;  // chunks per thread
+  static constexpr int RSTEP = NT / CPR;       // rows between a thread's chunks
+  static_assert((ROWS * CPR) % NT == 0 && NT % CPR == 0, "tile must split evenly");
+  u32x4 r[PER];
+  uint32_t goff;  // byte offset of the thread's first chunk in the global tile
+  uint32_t loff;  // element offset of the thread's first chunk in the LDS tile
+  int row;        // row of the thread's first chunk
 
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int valid, int tid) {
+  __device__ __forceinline__ void init(int tid, int ld) {
+    row = tid / CPR;
+    goff = (uint32_t)(row * D + 8 * (tid % CPR)) * 2u;
+    loff = (uint32_t)(row * ld + 8 * (tid % CPR));
+  }
+
+  // src: first element of the tile (uniform across the workgroup).
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int valid) {
+    const char* base = reinterpret_cast<const char*>(src) + goff;
+    if (valid >= ROWS) {
+#pragma unroll
+      for (int p = 0; p < PER; ++p)
+        r[p] = *reinterpret_cast<const u32x4*>(base + p * RSTEP * D * 2);
+      return;
+    }
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int mb = tid + p * NT;
-      const int cq = mb % CQ, rq = mb / CQ;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * rq + i;
-        if (row < valid) {
-          r[p][i] = *reinterpret_cast<const u32x2*>(src + (size_t)row * D + 4 * cq);
-        } else {
-          r[p][i] = u32x2{0u, 0u};
-        }
+      if (row + p * RSTEP < valid) {
+        r[p] = *reinterpret_cast<const u32x4*>(base + p * RSTEP * D * 2);
+      } else {
+        r[p] = u32x4{0u, 0u, 0u, 0u};
       }
     }
   }
 
-  __device__ __forceinline__ void store_rowmajor(uint16_t* dst, int ld, int tid) const {
+  __device__ __forceinline__ void store(uint16_t* dst, int ld) const {
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int mb = tid + p * NT;
-      const int cq = mb % CQ, rq = mb / CQ;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<u32x2*>(dst + (4 * rq + i) * ld + 4 * cq) = r[p][i];
-    }
-  }
-
-  __device__ __forceinline__ void store_transposed(uint16_t* dst, int ld, int tid) const {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int mb = tid + p * NT;
-      const int cq = mb % CQ, rq = mb / CQ;
-      const u32x2* a = r[p];
-      // column j of the micro-block: elements (row 0..3, col j)
-      u32x2 c0 = {(a[0][0] & 0xffffu) | (a[1][0] << 16), (a[2][0] & 0xffffu) | (a[3][0] << 16)};
-      u32x2 c1 = {(a[0][0] >> 16) | (a[1][0] & 0xffff0000u), (a[2][0] >> 16) | (a[3][0] & 0xffff0000u)};
-      u32x2 c2 = {(a[0][1] & 0xffffu) | (a[1][1] << 16), (a[2][1] & 0xffffu) | (a[3][1] << 16)};
-      u32x2 c3 = {(a[0][1] >> 16) | (a[1][1] & 0xffff0000u), (a[2][1] >> 16) | (a[3][1] & 0xffff0000u)};
-      uint16_t* base = dst + (4 * cq) * ld + 4 * rq;
-      *reinterpret_cast<u32x2*>(base + 0 * ld) = c0;
-      *reinterpret_cast<u32x2*>(base + 1 * ld) = c1;
-      *reinterpret_cast<u32x2*>(base + 2 * ld) = c2;
-      *reinterpret_cast<u32x2*>(base + 3 * ld) = c3;
-    }
+    for (int p = 0; p < PER; ++p)
+      *reinterpret_cast<u32x4*>(dst + loff + p * RSTEP * ld) = r[p];
   }
 };
 
