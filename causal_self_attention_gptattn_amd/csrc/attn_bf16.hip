@@ -44,7 +44,6 @@ namespace {
 constexpr int kThreads = 256;  // 4 waves
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max is moved
 
-__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
 
 // ---------------------------------------------------------------------------
 // Forward
@@ -76,7 +75,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb,
     float mx = st[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
-    mx = fmaxf(mx, wave_xor32(mx)) * sl2;
+    mx = half_max(mx) * sl2;
     // Lazy rescaling: the reference max m only moves when some row of the
     // wave sees a score more than 2^kLazy above it.  Until then the
     // probabilities exp2(s - m) stay below 2^kLazy, which bf16 and the
@@ -188,7 +187,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
     __syncthreads();
   }
 
-  const float lt = l + wave_xor32(l);
+  const float lt = half_sum(l);
   if (qi < T) {
     const float inv = 1.0f / lt;
     uint16_t* orow = O + ((size_t)n * T + qi) * D;
@@ -297,7 +296,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void attn_bwd_dq(
       df[s] = qf[s];
     }
   }
-  const float delta = dpart + wave_xor32(dpart);
+  const float delta = half_sum(dpart);
   const float nl = qi < T ? -LSE[(size_t)n * T + qi] * kLog2e : 0.0f;
   if (qi < T && g == 0) Delta[(size_t)n * T + qi] = delta;
   f32x16 nd;

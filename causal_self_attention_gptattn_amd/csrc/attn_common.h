@@ -54,6 +54,20 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(const float* p) {
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// Reductions across the two 32-lane halves of a wave (lane l with l ^ 32)
+// with v_permlane32_swap: after the swap, lane l holds x[l] and x[l ^ 32]
+// in the two results, in some order, which is all a symmetric op needs.
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
