@@ -360,29 +360,28 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void attn_bwd_dq(
 // Backward, part 2: dK and dV (lane -> key layout)
 // ---------------------------------------------------------------------------
 
+// Query-row statistics in LDS are stored permuted so that the 16 rows a
+// lane half needs for one 32-query block (rows 8u + 4g + i in result-
+// register order r = 4u + i) are contiguous: row q of the tile goes to
+// slot 32 (q / 32) + 16 ((q % 8) / 4) + 4 ((q % 32) / 8) + q % 4.
+__device__ __forceinline__ int stat_slot(int q) {
+  return 32 * (q >> 5) + 16 * ((q & 7) >> 2) + 4 * ((q & 31) >> 3) + (q & 3);
+}
+
 // One BM-query tile for one wave (32 keys, one per lane column c).  ls/es
-// hold lse * log2(e) and delta of the tile's queries.
+// hold -lse * log2(e) and -delta of the tile's queries, permuted by
+// stat_slot; -delta seeds the dP accumulator so that the product yields
+// dP - delta directly.
 template <int D, int BM, bool MASK>
 __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db, const float* ls,
                                           const float* es, const bf16x8* kf, const bf16x8* vf,
                                           f32x16* dvt, f32x16* dkt, int q0, int kj, int g,
                                           int c, int tro, float sl2) {
   constexpr int LD = D + 8, DS = D / 16, DE = D / 32, NH = BM / 32;
-  bf16x8 pf[NH][2], sf[NH][2];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-    // per-row statistics of rows 32h + 8u + 4g + i, in result-register order
-    f32x16 nl, nd;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const f32x4 lq = *reinterpret_cast<const f32x4*>(ls + 32 * h + 8 * u + 4 * g);
-      const f32x4 eq = *reinterpret_cast<const f32x4*>(es + 32 * h + 8 * u + 4 * g);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        nl[4 * u + i] = lq[i];
-        nd[4 * u + i] = -eq[i];
-      }
-    }
+    const f32x16 nl = *reinterpret_cast<const f32x16*>(ls + 32 * h + 16 * g);
+    const f32x16 nd = *reinterpret_cast<const f32x16*>(es + 32 * h + 16 * g);
     // S = Q K^T and dP - delta = dO V^T - delta: rows = queries, columns = keys
     f32x16 st = mfma32x32x16(ld_frag16(qb + (32 * h + c) * LD + 8 * g), kf[0], zero16());
     f32x16 dp = mfma32x32x16(ld_frag16(db + (32 * h + c) * LD + 8 * g), vf[0], nd);
@@ -391,32 +390,31 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
       st = mfma32x32x16(ld_frag16(qb + (32 * h + c) * LD + 16 * s + 8 * g), kf[s], st);
       dp = mfma32x32x16(ld_frag16(db + (32 * h + c) * LD + 16 * s + 8 * g), vf[s], dp);
     }
+    bf16x8 pf[2], sf[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       float p[8], dsv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = 8 * t + j;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sl2, -nl[r]));
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sl2, nl[r]));
         if (MASK && kj > q0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3)) pv = 0.0f;
         p[j] = pv;
         dsv[j] = pv * dp[r];
       }
-      pf[h][t] = pack_bf16x8(p);
-      sf[h][t] = pack_bf16x8(dsv);
+      pf[t] = pack_bf16x8(p);
+      sf[t] = pack_bf16x8(dsv);
     }
-  }
-  // dV^T += dO^T P and dK^T += Q^T dS, dO^T and Q^T read transposed
+    // dV^T += dO^T P and dK^T += Q^T dS, dO^T and Q^T read transposed
 #pragma unroll
-  for (int e = 0; e < DE; ++e)
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
+    for (int e = 0; e < DE; ++e)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int off = (32 * h + 16 * t) * LD + 32 * e + tro;
-        dvt[e] = mfma32x32x16(ld_frag_tr(db + off, LD), pf[h][t], dvt[e]);
-        dkt[e] = mfma32x32x16(ld_frag_tr(qb + off, LD), sf[h][t], dkt[e]);
+        dvt[e] = mfma32x32x16(ld_frag_tr(db + off, LD), pf[t], dvt[e]);
+        dkt[e] = mfma32x32x16(ld_frag_tr(qb + off, LD), sf[t], dkt[e]);
       }
+  }
 }
 
 template <int D, int BM>
@@ -432,8 +430,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
   constexpr int DE = D / 32;
   __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BM * LD];
   __shared__ __attribute__((aligned(16))) uint16_t Ds[2][BM * LD];
-  __shared__ __attribute__((aligned(16))) float Ls[2][BM];
-  __shared__ __attribute__((aligned(16))) float Es[2][BM];
+  __shared__ __attribute__((aligned(64))) float Ls[2][BM];
+  __shared__ __attribute__((aligned(64))) float Es[2][BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -475,16 +473,16 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
     ds.load(Dh + (size_t)q1 * D, T - q1);
     if (tid < BM) {
       const int q = q1 + tid;
-      lv = q < T ? LSE[rows + q] * kLog2e : INFINITY;
-      ev = q < T ? Delta[rows + q] : 0.0f;
+      lv = q < T ? -LSE[rows + q] * kLog2e : -INFINITY;
+      ev = q < T ? -Delta[rows + q] : 0.0f;
     }
   };
   auto store_tile = [&](int b) {
     qs.store(Qs[b], LD);
     ds.store(Ds[b], LD);
     if (tid < BM) {
-      Ls[b][tid] = lv;
-      Es[b][tid] = ev;
+      Ls[b][stat_slot(tid)] = lv;
+      Es[b][stat_slot(tid)] = ev;
     }
   };
   load_tile(qt0);
