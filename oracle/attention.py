@@ -53,48 +53,73 @@ def _heads(B, H, heads):
     return [tuple(bh) for bh in heads]
 
 
-def scores(q, k, scale):
-    """Masked, scaled score matrix S for one (batch, head): ``[T, T]``.
+def visible(Tq, Tk, offset=0, window=0):
+    """Boolean ``[Tq, Tk]`` matrix of the (query, key) pairs that attend.
 
-    Entries above the diagonal (keys in the future of the query) are -inf.
+    Query i sees key j when j <= i + offset (nothing from its future); with
+    window > 0 it also needs j > i + offset - window (a local band of the
+    `window` most recent positions, the "locally banded" layers of GPT-3 in
+    the minGPT README notes).  offset = Tk - Tq lines the last query up with
+    the last key (new tokens appended to a context).  offset = 0, window = 0,
+    Tq = Tk is the plain causal mask.
+    """
+    i = np.arange(Tq)[:, None] + offset
+    j = np.arange(Tk)[None, :]
+    ok = j <= i
+    if window > 0:
+        ok &= j > i - window
+    return ok
+
+
+def scores(q, k, scale, offset=0, window=0):
+    """Masked, scaled score matrix S for one (batch, head): ``[Tq, Tk]``.
+
+    Entries of keys a query may not see are -inf (for plain causal
+    attention: everything above the diagonal).
     """
     q = _as_f64(q)
     k = _as_f64(k)
-    T = q.shape[0]
     s = _scale64(scale) * (q @ k.T)
-    future = np.triu(np.ones((T, T), dtype=bool), k=1)
-    s[future] = -np.inf
+    s[~visible(q.shape[0], k.shape[0], offset, window)] = -np.inf
     return s
 
 
-def probabilities(q, k, scale):
-    """Row softmax of the masked scores for one (batch, head): ``[T, T]``."""
-    s = scores(q, k, scale)
+def _softmax_rows(s):
+    """Row softmax; a row with no visible key gets all-zero weights."""
     m = s.max(axis=1, keepdims=True)
-    e = np.exp(s - m)
-    return e / e.sum(axis=1, keepdims=True)
-
-
-def forward_head(q, k, v, scale):
-    """One (batch, head): returns ``(O [T, D], lse [T])`` in float64."""
-    s = scores(q, k, scale)
-    m = s.max(axis=1, keepdims=True)
+    empty = ~np.isfinite(m[:, 0])
+    m[empty] = 0.0
     e = np.exp(s - m)
     l = e.sum(axis=1, keepdims=True)
-    p = e / l
+    p = np.divide(e, l, out=np.zeros_like(e), where=l > 0)
+    lse = np.where(empty, -np.inf, (m + np.log(np.where(l > 0, l, 1.0)))[:, 0])
+    return p, lse
+
+
+def probabilities(q, k, scale, offset=0, window=0):
+    """Row softmax of the masked scores for one (batch, head)."""
+    return _softmax_rows(scores(q, k, scale, offset, window))[0]
+
+
+def forward_head(q, k, v, scale, offset=0, window=0):
+    """One (batch, head): returns ``(O [Tq, D], lse [Tq])`` in float64.
+
+    A query row that sees no key (possible only with a negative offset) has
+    O = 0 and lse = -inf.
+    """
+    p, lse = _softmax_rows(scores(q, k, scale, offset, window))
     o = p @ _as_f64(v)
-    lse = (m + np.log(l))[:, 0]
     return o, lse
 
 
-def backward_head(q, k, v, do, scale):
-    """One (batch, head): returns ``(dQ, dK, dV)``, each ``[T, D]`` float64."""
+def backward_head(q, k, v, do, scale, offset=0, window=0):
+    """One (batch, head): returns ``(dQ [Tq, D], dK [Tk, D], dV [Tk, D])``."""
     q = _as_f64(q)
     k = _as_f64(k)
     v = _as_f64(v)
     do = _as_f64(do)
     sc = _scale64(scale)
-    p = probabilities(q, k, scale)
+    p = probabilities(q, k, scale, offset, window)
     dv = p.T @ do
     dp = do @ v.T
     row = (p * dp).sum(axis=1, keepdims=True)
@@ -104,33 +129,35 @@ def backward_head(q, k, v, do, scale):
     return dq, dk, dv
 
 
-def forward(q, k, v, scale, heads=None):
-    """Batched forward over ``[B, H, T, D]`` inputs.
+def forward(q, k, v, scale, heads=None, offset=0, window=0):
+    """Batched forward over ``[B, H, Tq, D]`` queries and ``[B, H, Tk, D]``
+    keys/values.
 
     ``heads`` optionally lists the (b, h) pairs to compute; the others are
     left as NaN so that a caller cannot mistake them for results.
-    Returns ``(O [B,H,T,D], lse [B,H,T])`` in float64.
+    Returns ``(O [B,H,Tq,D], lse [B,H,Tq])`` in float64.
     """
     q = np.asarray(q)
-    B, H, T, D = q.shape
-    o = np.full((B, H, T, D), np.nan)
-    lse = np.full((B, H, T), np.nan)
+    B, H, Tq, D = q.shape
+    o = np.full((B, H, Tq, D), np.nan)
+    lse = np.full((B, H, Tq), np.nan)
     for b, h in _heads(B, H, heads):
-        o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], scale)
+        o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], scale, offset, window)
     return o, lse
 
 
-def backward(q, k, v, do, scale, heads=None):
-    """Batched backward; returns ``(dQ, dK, dV)`` as ``[B,H,T,D]`` float64.
-
-    Heads not listed in ``heads`` are NaN.
+def backward(q, k, v, do, scale, heads=None, offset=0, window=0):
+    """Batched backward; returns ``(dQ, dK, dV)`` in float64 (dQ like q,
+    dK and dV like k).  Heads not listed in ``heads`` are NaN.
     """
     q = np.asarray(q)
-    B, H, T, D = q.shape
-    dq = np.full((B, H, T, D), np.nan)
-    dk = np.full((B, H, T, D), np.nan)
-    dv = np.full((B, H, T, D), np.nan)
+    k = np.asarray(k)
+    B, H, Tq, D = q.shape
+    Tk = k.shape[2]
+    dq = np.full((B, H, Tq, D), np.nan)
+    dk = np.full((B, H, Tk, D), np.nan)
+    dv = np.full((B, H, Tk, D), np.nan)
     for b, h in _heads(B, H, heads):
         dq[b, h], dk[b, h], dv[b, h] = backward_head(
-            q[b, h], k[b, h], v[b, h], do[b, h], scale)
+            q[b, h], k[b, h], v[b, h], do[b, h], scale, offset, window)
     return dq, dk, dv

@@ -13,21 +13,33 @@ loops; "version 3" turns masked affinities into weights with a softmax;
 correction fixes that only past and present positions are visible.
 
 Inputs are nested lists indexed ``[b][h][t][d]``; so are the outputs
-(``lse`` is ``[b][h][t]``).
+(``lse`` is ``[b][h][t]``).  The optional ``offset`` and ``window`` select
+which keys a query sees exactly as in :func:`oracle.attention.visible`.
 """
 
 import math
 
 
-def _head_forward(q, k, v, scale):
-    T = len(q)
+def _keys(i, Tk, offset, window):
+    """Keys query i may look at: j <= i + offset, and j > i + offset - window
+    when a window is set; never the future."""
+    hi = min(Tk - 1, i + offset)
+    lo = max(0, i + offset - window + 1) if window > 0 else 0
+    return list(range(lo, hi + 1))
+
+
+def _head_forward(q, k, v, scale, offset=0, window=0):
     D = len(q[0])
     o = []
     lse = []
-    for i in range(T):
-        # affinities with keys 0..i only: the future is never looked at
+    for i in range(len(q)):
+        keys = _keys(i, len(k), offset, window)
+        if not keys:
+            o.append([0.0] * D)
+            lse.append(-math.inf)
+            continue
         s = []
-        for j in range(i + 1):
+        for j in keys:
             acc = 0.0
             for d in range(D):
                 acc += q[i][d] * k[j][d]
@@ -40,23 +52,25 @@ def _head_forward(q, k, v, scale):
         row = []
         for d in range(D):
             acc = 0.0
-            for j in range(i + 1):
-                acc += w[j] * v[j][d]
+            for n, j in enumerate(keys):
+                acc += w[n] * v[j][d]
             row.append(acc / z)
         o.append(row)
         lse.append(m + math.log(z))
     return o, lse
 
 
-def _head_backward(q, k, v, do, scale):
-    T = len(q)
+def _head_backward(q, k, v, do, scale, offset=0, window=0):
     D = len(q[0])
-    dq = [[0.0] * D for _ in range(T)]
-    dk = [[0.0] * D for _ in range(T)]
-    dv = [[0.0] * D for _ in range(T)]
-    for i in range(T):
+    dq = [[0.0] * D for _ in range(len(q))]
+    dk = [[0.0] * D for _ in range(len(k))]
+    dv = [[0.0] * D for _ in range(len(k))]
+    for i in range(len(q)):
+        keys = _keys(i, len(k), offset, window)
+        if not keys:
+            continue
         s = []
-        for j in range(i + 1):
+        for j in keys:
             acc = 0.0
             for d in range(D):
                 acc += q[i][d] * k[j][d]
@@ -69,18 +83,18 @@ def _head_backward(q, k, v, do, scale):
         p = [x / z for x in w]
         # o_i = sum_j p_ij v_j, so dL/dp_ij = do_i . v_j and dL/dv_j += p_ij do_i
         g = []
-        for j in range(i + 1):
+        for n, j in enumerate(keys):
             acc = 0.0
             for d in range(D):
                 acc += do[i][d] * v[j][d]
-                dv[j][d] += p[j] * do[i][d]
+                dv[j][d] += p[n] * do[i][d]
             g.append(acc)
         # softmax: dL/ds_ij = p_ij (g_ij - sum_k p_ik g_ik)
         mean = 0.0
-        for j in range(i + 1):
-            mean += p[j] * g[j]
-        for j in range(i + 1):
-            ds = p[j] * (g[j] - mean)
+        for n in range(len(keys)):
+            mean += p[n] * g[n]
+        for n, j in enumerate(keys):
+            ds = p[n] * (g[n] - mean)
             # s_ij = scale * q_i . k_j
             for d in range(D):
                 dq[i][d] += scale * ds * k[j][d]
@@ -88,13 +102,13 @@ def _head_backward(q, k, v, do, scale):
     return dq, dk, dv
 
 
-def forward(q, k, v, scale):
+def forward(q, k, v, scale, offset=0, window=0):
     """Returns ``(o, lse)`` as nested lists."""
     o, lse = [], []
     for b in range(len(q)):
         ob, lb = [], []
         for h in range(len(q[b])):
-            oh, lh = _head_forward(q[b][h], k[b][h], v[b][h], scale)
+            oh, lh = _head_forward(q[b][h], k[b][h], v[b][h], scale, offset, window)
             ob.append(oh)
             lb.append(lh)
         o.append(ob)
@@ -102,13 +116,13 @@ def forward(q, k, v, scale):
     return o, lse
 
 
-def backward(q, k, v, do, scale):
+def backward(q, k, v, do, scale, offset=0, window=0):
     """Returns ``(dq, dk, dv)`` as nested lists for L = sum(O * dO)."""
     dq, dk, dv = [], [], []
     for b in range(len(q)):
         qb, kb, vb = [], [], []
         for h in range(len(q[b])):
-            a, c, e = _head_backward(q[b][h], k[b][h], v[b][h], do[b][h], scale)
+            a, c, e = _head_backward(q[b][h], k[b][h], v[b][h], do[b][h], scale, offset, window)
             qb.append(a)
             kb.append(c)
             vb.append(e)
