@@ -17,6 +17,13 @@ dimension per EX1):
 
 Tensors are ``[B, H, T, D]`` contiguous, bfloat16 (D in {64, 128}) or
 float32 (D in {16, 32, 64}); ``lse`` is ``[B, H, T]`` float32.
+
+The ``*_ex`` calls take any ``[B, H, T, D]`` view whose last dimension is
+contiguous (for example q, k and v sliced out of one packed ``[B, T, 3C]``
+projection output, see :func:`split_qkv`), allow ``Tq != Tk`` and take the
+two mask parameters of ``gptattn_problem``: query i sees key j when
+``j <= i + causal_offset`` and, with ``window > 0``, ``j > i + causal_offset
+- window``.
 """
 
 import ctypes
@@ -26,8 +33,9 @@ import os
 import torch
 
 __all__ = [
-    "fwd", "bwd", "bwd_dq", "bwd_dkdv", "attention", "GPTAttnFunction", "workspace_bytes",
-    "status_string", "version", "library", "LIB_PATH",
+    "fwd", "bwd", "bwd_dq", "bwd_dkdv", "fwd_ex", "bwd_ex", "split_qkv", "attention",
+    "GPTAttnFunction", "workspace_bytes", "ex_workspace_bytes", "status_string", "version",
+    "library", "LIB_PATH", "Tensor", "Problem", "DTYPE_BF16", "DTYPE_F32",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptattn.so")
@@ -37,6 +45,27 @@ _p = ctypes.c_void_p
 _i = ctypes.c_int
 _f = ctypes.c_float
 _sz = ctypes.c_size_t
+
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+
+
+class Tensor(ctypes.Structure):
+    """``gptattn_tensor``: element (b, h, t, d) at data + b*stride_b +
+    h*stride_h + t*stride_t + d (elements)."""
+    _fields_ = [("data", ctypes.c_void_p), ("stride_b", ctypes.c_longlong),
+                ("stride_h", ctypes.c_longlong), ("stride_t", ctypes.c_longlong)]
+
+
+class Problem(ctypes.Structure):
+    """``gptattn_problem``."""
+    _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("Tq", ctypes.c_int),
+                ("Tk", ctypes.c_int), ("D", ctypes.c_int), ("causal_offset", ctypes.c_int),
+                ("window", ctypes.c_int), ("scale", ctypes.c_float), ("dtype", ctypes.c_int)]
+
+
+_tp = ctypes.POINTER(Tensor)
+_pp = ctypes.POINTER(Problem)
 
 # name -> (restype, argtypes); mirrors include/gptattn.h
 SIGNATURES = {
@@ -50,6 +79,9 @@ SIGNATURES = {
                                   _p]),
     "gptattn_bwd_f32": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p, _sz, _p]),
     "gptattn_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "gptattn_fwd_ex": (_i, [_pp, _tp, _tp, _tp, _tp, _p, _p]),
+    "gptattn_bwd_ex": (_i, [_pp, _tp, _tp, _tp, _tp, _tp, _p, _tp, _tp, _tp, _p, _sz, _p]),
+    "gptattn_bwd_ex_workspace_bytes": (_sz, [_pp]),
     "gptattn_status_string": (ctypes.c_char_p, [_i]),
     "gptattn_version": (_i, []),
 }
@@ -214,23 +246,124 @@ def bwd_dkdv(q, k, v, do, lse, workspace, scale=None, dk=None, dv=None):
     return dk, dv
 
 
+# ---------------------------------------------------------------------------
+# Strided views, Tq != Tk, shifted and banded masks (gptattn_*_ex)
+# ---------------------------------------------------------------------------
+
+def split_qkv(x, n_head):
+    """Views q, k, v ``[B, H, T, D]`` of a packed ``[B, T, 3C]`` projection
+    output (q, k, v concatenated along the last axis, each C = H*D wide,
+    heads in order), without copying."""
+    B, T, C3 = x.shape
+    C = C3 // 3
+    xv = x.view(B, T, 3, n_head, C // n_head)
+    return tuple(xv[:, :, i].transpose(1, 2) for i in range(3))
+
+
+def _tensor(t):
+    if t.stride(3) != 1:
+        raise ValueError("the last (head) dimension must be contiguous")
+    st = [0 if t.shape[i] == 1 else t.stride(i) for i in range(3)]
+    return Tensor(t.data_ptr(), st[0], st[1], st[2])
+
+
+def _problem(q, k, scale, causal_offset, window):
+    B, H, Tq, D = q.shape
+    dt = DTYPE_F32 if q.dtype == torch.float32 else DTYPE_BF16
+    return Problem(B, H, Tq, k.shape[2], D, int(causal_offset), int(window),
+                   _scale(scale, D), dt)
+
+
+def _validate_ex(q, k, v, *rows_q):
+    for t in (q, k, v) + rows_q:
+        if t.dim() != 4:
+            raise ValueError("expected [B, H, T, D] tensors, got shape %s" % (tuple(t.shape),))
+        if not t.is_cuda or t.device != q.device:
+            raise ValueError("tensors must live on the same GPU")
+        if t.dtype != q.dtype or q.dtype not in (torch.bfloat16, torch.float32):
+            raise ValueError("tensors must all be bfloat16 or all float32")
+    B, H, Tq, D = q.shape
+    if k.shape != v.shape or k.shape[:2] != (B, H) or k.shape[3] != D:
+        raise ValueError("k and v must be [B, H, Tk, D] with q's B, H and D")
+    for t in rows_q:
+        if t.shape != q.shape:
+            raise ValueError("o, dO and dq must have q's shape")
+
+
+def ex_workspace_bytes(q, k, scale=None, causal_offset=0, window=0):
+    pb = _problem(q, k, scale, causal_offset, window)
+    return library().gptattn_bwd_ex_workspace_bytes(ctypes.byref(pb))
+
+
+def fwd_ex(q, k, v, scale=None, causal_offset=0, window=0, out=None, lse=None):
+    """Forward pass over strided ``[B, H, T, D]`` views; returns ``(o, lse)``.
+
+    ``out`` may be any view of q's shape with a contiguous last dimension
+    (for example a ``[B, T, H, D]`` buffer transposed to ``[B, H, T, D]``).
+    """
+    _validate_ex(q, k, v)
+    B, H, Tq, D = q.shape
+    out = torch.empty_like(q, memory_format=torch.contiguous_format) if out is None else out
+    lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _validate_ex(q, k, v, out)
+    _rows_ok(lse, q)
+    pb = _problem(q, k, scale, causal_offset, window)
+    ts = [_tensor(t) for t in (q, k, v, out)]
+    with torch.cuda.device(q.device):
+        rc = library().gptattn_fwd_ex(ctypes.byref(pb), *[ctypes.byref(t) for t in ts],
+                                      _ptr(lse), _stream(q.device))
+    _check(rc, "gptattn_fwd_ex")
+    return out, lse
+
+
+def bwd_ex(q, k, v, o, do, lse, scale=None, causal_offset=0, window=0, dq=None, dk=None,
+           dv=None, workspace=None):
+    """Backward pass over strided views; returns ``(dq, dk, dv)``.  The
+    gradients may be views into one packed buffer (see :func:`split_qkv`)."""
+    _validate_ex(q, k, v, o, do)
+    _rows_ok(lse, q)
+    fresh = dict(memory_format=torch.contiguous_format)
+    dq = torch.empty_like(q, **fresh) if dq is None else dq
+    dk = torch.empty_like(k, **fresh) if dk is None else dk
+    dv = torch.empty_like(v, **fresh) if dv is None else dv
+    _validate_ex(q, dk, dv, dq)
+    pb = _problem(q, k, scale, causal_offset, window)
+    lib = library()
+    need = lib.gptattn_bwd_ex_workspace_bytes(ctypes.byref(pb))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ts = [_tensor(t) for t in (q, k, v, o, do)]
+    gs = [_tensor(t) for t in (dq, dk, dv)]
+    with torch.cuda.device(q.device):
+        rc = lib.gptattn_bwd_ex(ctypes.byref(pb), *[ctypes.byref(t) for t in ts], _ptr(lse),
+                                *[ctypes.byref(t) for t in gs], _ptr(workspace),
+                                workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check(rc, "gptattn_bwd_ex")
+    return dq, dk, dv
+
+
 class GPTAttnFunction(torch.autograd.Function):
-    """Autograd wrapper: saves (q, k, v, o, lse) and calls :func:`bwd`."""
+    """Autograd wrapper: saves (q, k, v, o, lse) and calls the backward
+    launches.  Inputs may be strided views (for example from
+    :func:`split_qkv`)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, scale=None):
-        o, lse = fwd(q, k, v, scale)
+    def forward(ctx, q, k, v, scale=None, causal_offset=0, window=0):
+        o, lse = fwd_ex(q, k, v, scale, causal_offset, window)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.scale = scale
+        ctx.args = (scale, causal_offset, window)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = bwd(q, k, v, o, do.contiguous(), lse, ctx.scale)
-        return dq, dk, dv, None
+        if do.stride(3) != 1:
+            do = do.contiguous()
+        dq, dk, dv = bwd_ex(q, k, v, o, do, lse, *ctx.args)
+        return dq, dk, dv, None, None, None
 
 
-def attention(q, k, v, scale=None):
-    """Differentiable causal self-attention over ``[B, H, T, D]`` tensors."""
-    return GPTAttnFunction.apply(q, k, v, scale)
+def attention(q, k, v, scale=None, causal_offset=0, window=0):
+    """Differentiable causal self-attention over ``[B, H, T, D]`` views
+    (``Tq`` queries, ``Tk`` keys; mask parameters as in :func:`fwd_ex`)."""
+    return GPTAttnFunction.apply(q, k, v, scale, causal_offset, window)

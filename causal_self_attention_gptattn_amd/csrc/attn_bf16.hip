@@ -5,32 +5,35 @@
 // code, spelled out": chapters "version 3: adding softmax" and "version 4:
 // self-attention", note 6 and the corrections at 00:57:00 and 01:20:05; heads
 // as a batch dimension per exercise EX1 and "batched multi-headed
-// self-attention"):  O = softmax(scale Q K^T, keys j <= i only) V, with the
-// natural-log normaliser lse kept for the backward pass.
+// self-attention"):  O = softmax(scale Q K^T over the visible keys) V, with
+// the natural-log normaliser lse kept for the backward pass.  Visibility is
+// the causal rule, optionally shifted by an offset (queries appended to a
+// longer context) and limited to a band of recent positions (the "locally
+// banded" layers of GPT-3 in the minGPT README notes); see attn_common.h.
 //
 // Kernels (one wave = 64 lanes; every product is v_mfma_f32_32x32x16_bf16,
 // see attn_common.h for the register layout):
 //
 //   attn_fwd      one workgroup = 128 queries of one head (4 waves x 32).
-//                 Walks key tiles of 64 from position 0 up to the diagonal;
-//                 tiles above the diagonal are never visited and only tiles
-//                 that straddle it are masked.  Scores are formed transposed,
-//                 S^T = K Q^T, so that each lane owns one query: the online
-//                 softmax (running max m and sum l) stays in registers, the
-//                 row reductions need one cross-half exchange, and the bf16
-//                 probabilities feed O^T += V^T P^T straight from registers.
-//                 K and V are staged row-major in LDS; V^T is read with
-//                 the gfx950 transpose read (attn_common.h).
+//                 Walks only the 64-key tiles its rows can see and masks
+//                 only the tiles that straddle the edge of visibility.
+//                 Scores are formed transposed, S^T = K Q^T, so that each
+//                 lane owns one query: the online softmax (running max m and
+//                 sum l) stays in registers, the row reductions need one
+//                 cross-half exchange, and the bf16 probabilities feed
+//                 O^T += V^T P^T straight from registers.  K and V are staged
+//                 row-major in LDS; V^T is read with the gfx950 transpose
+//                 read (attn_common.h).
 //   attn_bwd_dq   same tiling as attn_fwd.  First forms the row term
 //                 delta_i = sum_d dO_id O_id (written to the workspace for
 //                 attn_bwd_dkdv), then recomputes P^T from lse, dP^T = V dO^T,
 //                 dS^T = P^T (dP^T - delta) and dQ^T += K^T dS^T.
 //   attn_bwd_dkdv one workgroup = 128 keys of one head (4 waves x 32).  Walks
-//                 query tiles from the diagonal to the end with the lane ->
-//                 key layout: S = Q K^T and dP = dO V^T, then
-//                 dV^T += dO^T P and dK^T += Q^T dS with P and dS taken from
-//                 registers.  Q and dO are staged row-major in LDS and
-//                 read transposed for the dV/dK products.
+//                 the query tiles that see its keys with the lane -> key
+//                 layout: S = Q K^T and dP = dO V^T, then dV^T += dO^T P and
+//                 dK^T += Q^T dS with P and dS taken from registers.  Q and dO
+//                 are staged row-major in LDS and read transposed for the
+//                 dV/dK products.
 //
 // dQ and dK/dV come from separate kernels, so no result is accumulated with
 // atomics and every output is bitwise reproducible run to run.
@@ -43,7 +46,24 @@ namespace {
 
 constexpr int kThreads = 256;  // 4 waves
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max is moved
+constexpr int kBM = 128;       // queries per forward / dQ workgroup
+constexpr int kBN = 64;        // keys per staged K/V tile
+constexpr int kKBN = 128;      // keys per dK/dV workgroup
 
+// Key tiles [t0, t1] a query range sees (t1 < t0 when none).
+struct TileSpan {
+  int t0, t1;
+};
+__device__ __forceinline__ TileSpan key_tiles(int i0, int i1, const Problem& pb, int bn) {
+  const int lo = keys_lo(i0, pb), hi = i0 < pb.Tq ? keys_hi(min(i1, pb.Tq - 1), pb) : -1;
+  return TileSpan{lo / bn, hi >= lo ? hi / bn : lo / bn - 1};
+}
+
+// Does some query in [i0, i1] fail to see some key in [j0, j1]?  Only such
+// tiles pay for the element-wise mask.
+__device__ __forceinline__ bool needs_mask(int i0, int i1, int j0, int j1, const Problem& pb) {
+  return j1 > i0 + pb.off || j1 >= pb.Tk || (pb.win > 0 && j0 <= i1 + pb.off - pb.win);
+}
 
 // ---------------------------------------------------------------------------
 // Forward
@@ -51,12 +71,12 @@ constexpr float kLazy = 8.0f;  // log2 headroom before the running max is moved
 
 // One 64-key tile for one wave (32 queries, one per lane column c), taken
 // as two 32-key halves with one online-softmax step each, which keeps only
-// half a tile of scores live.  MASK is set only for tiles that straddle the
-// diagonal (or the end of the sequence).
+// half a tile of scores live.  A row that has seen no key yet keeps
+// m = -inf; the guards keep -inf from meeting -inf.
 template <int D, bool MASK>
 __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf,
-                                         f32x16* ot, float& m, float& l, int k0, int qi, int c,
-                                         int g, int tro, float sl2) {
+                                         f32x16* ot, float& m, float& l, int k0, Span seen, int c,
+                                         int g, int tro, const Problem& pb) {
   constexpr int LD = D + 8, DS = D / 16, DE = D / 32;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
@@ -69,13 +89,13 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb,
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = k0 + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (key > qi) st[r] = -INFINITY;
+        if (!inside(key, seen)) st[r] = -INFINITY;
       }
     }
     float mx = st[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, st[r]);
-    mx = half_max(mx) * sl2;
+    mx = half_max(mx) * pb.sl2;
     // Lazy rescaling: the reference max m only moves when some row of the
     // wave sees a score more than 2^kLazy above it.  Until then the
     // probabilities exp2(s - m) stay below 2^kLazy, which bf16 and the
@@ -83,20 +103,20 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb,
     // reference, so the final O / l is unchanged.
     if (__any(mx > m + kLazy)) {
       const float mnew = fmaxf(m, mx);
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+      const float alpha = m > -INFINITY ? __builtin_amdgcn_exp2f(m - mnew) : 0.0f;
       m = mnew;
       l *= alpha;
 #pragma unroll
       for (int e = 0; e < DE; ++e) ot[e] *= alpha;
     }
-    const float nm = -m;
+    const float nm = m > -INFINITY ? -m : 0.0f;
     bf16x8 pf[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       float p[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[8 * t + j], sl2, nm));
+        p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[8 * t + j], pb.sl2, nm));
         l += p[j];
       }
       pf[t] = pack_bf16x8(p);
@@ -113,10 +133,8 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb,
 
 template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, uint16_t* __restrict__ O,
-    float* __restrict__ LSE, int N, int T, float sl2, int nqb) {
-  constexpr int BM = 128, BN = 64;
+    View Q, View K, View V, View O, float* __restrict__ LSE, Problem pb, int nqb) {
+  constexpr int BM = kBM, BN = kBN;
   constexpr int LD = D + 8;     // padded row stride of the LDS tiles
   constexpr int DS = D / 16;    // k-steps of the score product
   constexpr int DE = D / 32;    // 32-row output tiles over the head dim
@@ -128,35 +146,44 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
   const int c = lane & 31, g = lane >> 5;
   const int tro = tr_rowoff(lane) * LD + tr_coloff(lane);
   const int bid = blockIdx.x;
-  const int qb = nqb - 1 - bid / N;  // longest query blocks first
-  const int n = bid % N;
-  const uint16_t* Kh = K + (size_t)n * T * D;
-  const uint16_t* Vh = V + (size_t)n * T * D;
+  const int qb = nqb - 1 - bid / pb.N;  // longest query blocks first
+  const int n = bid % pb.N;
+  const uint16_t* Kh = head_of(K, n, pb.H);
+  const uint16_t* Vh = head_of(V, n, pb.H);
   const int q0 = qb * BM;
   const int q0w = q0 + 32 * w;
   const int qi = q0w + c;
 
   bf16x8 qf[DS];
+  {
+    const uint16_t* qr = head_of(Q, n, pb.H) + (long long)qi * Q.st;
 #pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    if (qi < T) {
-      qf[s] = ld_frag16(Q + ((size_t)n * T + qi) * D + 16 * s + 8 * g);
-    } else {
-      qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    for (int s = 0; s < DS; ++s) {
+      if (qi < pb.Tq) {
+        qf[s] = ld_frag16(qr + 16 * s + 8 * g);
+      } else {
+        qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+      }
     }
   }
 
-  const int kend = min(q0 + BM, T);
-  const int nkt = (kend - 1) / BN + 1;
-  const int wnkt = q0w < T ? (min(q0w + 32, T) - 1) / BN + 1 : 0;
+  // key tiles seen by the workgroup's rows, and by this wave's rows
+  const TileSpan ws = key_tiles(q0, q0 + BM - 1, pb, BN);
+  const TileSpan wv = key_tiles(q0w, q0w + 31, pb, BN);
+  const int wlast = min(q0w + 31, pb.Tq - 1);
+  const Span seen = keys_of(qi, pb);  // keys this lane's query sees
 
   RowStage<BN, D, kThreads> ks, vs;
-  ks.init(tid, LD);
-  vs.init(tid, LD);
-  ks.load(Kh, T);
-  vs.load(Vh, T);
-  ks.store(Ks[0], LD);
-  vs.store(Vs[0], LD);
+  ks.init(tid, LD, K.st);
+  vs.init(tid, LD, V.st);
+  {  // first tile (reads nothing when the workgroup sees no key)
+    const int k1 = ws.t0 * BN;
+    const int valid = ws.t1 >= ws.t0 ? pb.Tk - k1 : 0;
+    ks.load(Kh + (long long)k1 * K.st, valid);
+    vs.load(Vh + (long long)k1 * V.st, valid);
+    ks.store(Ks[0], LD);
+    vs.store(Vs[0], LD);
+  }
   __syncthreads();
 
   f32x16 ot[DE];
@@ -164,20 +191,20 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
   for (int e = 0; e < DE; ++e) ot[e] = zero16();
   float m = -INFINITY, l = 0.0f;
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nkt;
+  for (int kt = ws.t0; kt <= ws.t1; ++kt) {
+    const int buf = (kt - ws.t0) & 1;
+    const bool more = kt < ws.t1;
     if (more) {
       const int k1 = (kt + 1) * BN;
-      ks.load(Kh + (size_t)k1 * D, T - k1);
-      vs.load(Vh + (size_t)k1 * D, T - k1);
+      ks.load(Kh + (long long)k1 * K.st, pb.Tk - k1);
+      vs.load(Vh + (long long)k1 * V.st, pb.Tk - k1);
     }
-    if (kt < wnkt) {
+    if (kt >= wv.t0 && kt <= wv.t1) {
       const int k0 = kt * BN;
-      if (k0 + BN - 1 > q0w) {
-        fwd_tile<D, true>(Ks[buf], Vs[buf], qf, ot, m, l, k0, qi, c, g, tro, sl2);
+      if (needs_mask(q0w, wlast, k0, k0 + BN - 1, pb)) {
+        fwd_tile<D, true>(Ks[buf], Vs[buf], qf, ot, m, l, k0, seen, c, g, tro, pb);
       } else {
-        fwd_tile<D, false>(Ks[buf], Vs[buf], qf, ot, m, l, k0, qi, c, g, tro, sl2);
+        fwd_tile<D, false>(Ks[buf], Vs[buf], qf, ot, m, l, k0, seen, c, g, tro, pb);
       }
     }
     if (more) {
@@ -188,9 +215,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
   }
 
   const float lt = half_sum(l);
-  if (qi < T) {
-    const float inv = 1.0f / lt;
-    uint16_t* orow = O + ((size_t)n * T + qi) * D;
+  if (qi < pb.Tq) {
+    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;  // a row that sees no key outputs 0
+    uint16_t* orow = const_cast<uint16_t*>(head_of(O, n, pb.H)) + (long long)qi * O.st;
 #pragma unroll
     for (int e = 0; e < DE; ++e)
 #pragma unroll
@@ -199,7 +226,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
                     pack_bf16x2(ot[e][4 * u + 2] * inv, ot[e][4 * u + 3] * inv)};
         *reinterpret_cast<u32x2*>(orow + 32 * e + 8 * u + 4 * g) = pk;
       }
-    if (g == 0) LSE[(size_t)n * T + qi] = (m + log2f(lt)) * kLn2;
+    if (g == 0)
+      LSE[(long long)n * pb.Tq + qi] = lt > 0.0f ? (m + log2f(lt)) * kLn2 : -INFINITY;
   }
 }
 
@@ -210,10 +238,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
 // One 64-key tile for one wave of the dQ kernel, taken as two 32-key
 // halves.  nd holds -delta of this lane's query in all 16 slots; it seeds
 // the dP^T accumulator so that the product directly yields dP^T - delta.
+// nl is -lse * log2(e), -inf for a row that sees no key (then P = 0).
 template <int D, bool MASK>
 __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf,
                                         const bf16x8* df, const f32x16& nd, f32x16* acc, int k0,
-                                        int qi, int c, int g, int tro, float sl2, float nl) {
+                                        Span seen, int c, int g, int tro, float nl,
+                                        const Problem& pb) {
   constexpr int LD = D + 8, DS = D / 16, DE = D / 32;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
@@ -232,10 +262,10 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = 8 * t + j;
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sl2, nl));
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], pb.sl2, nl));
         if (MASK) {
           const int key = k0 + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
-          if (key > qi) p = 0.0f;
+          if (!inside(key, seen)) p = 0.0f;
         }
         ds[j] = p * dp[r];
       }
@@ -253,12 +283,9 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
 
 template <int D>
 __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void attn_bwd_dq(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, const uint16_t* __restrict__ O,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE,
-    uint16_t* __restrict__ dQ, float* __restrict__ Delta, int N, int T,
-    float sl2, float scale, int nqb) {
-  constexpr int BM = 128, BN = 64;
+    View Q, View K, View V, View O, View dO, const float* __restrict__ LSE, View dQ,
+    float* __restrict__ Delta, Problem pb, int nqb) {
+  constexpr int BM = kBM, BN = kBN;
   constexpr int LD = D + 8;
   constexpr int DS = D / 16;
   constexpr int DE = D / 32;
@@ -270,70 +297,82 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void attn_bwd_dq(
   const int c = lane & 31, g = lane >> 5;
   const int tro = tr_rowoff(lane) * LD + tr_coloff(lane);
   const int bid = blockIdx.x;
-  const int qb = nqb - 1 - bid / N;
-  const int n = bid % N;
-  const uint16_t* Kh = K + (size_t)n * T * D;
-  const uint16_t* Vh = V + (size_t)n * T * D;
+  const int qb = nqb - 1 - bid / pb.N;
+  const int n = bid % pb.N;
+  const uint16_t* Kh = head_of(K, n, pb.H);
+  const uint16_t* Vh = head_of(V, n, pb.H);
   const int q0 = qb * BM;
   const int q0w = q0 + 32 * w;
   const int qi = q0w + c;
+  const long long row = (long long)n * pb.Tq + qi;
 
   bf16x8 qf[DS], df[DS];
   float dpart = 0.0f;
+  {
+    const uint16_t* qr = head_of(Q, n, pb.H) + (long long)qi * Q.st;
+    const uint16_t* dr = head_of(dO, n, pb.H) + (long long)qi * dO.st;
+    const uint16_t* orr = head_of(O, n, pb.H) + (long long)qi * O.st;
 #pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    if (qi < T) {
-      const size_t off = ((size_t)n * T + qi) * D + 16 * s + 8 * g;
-      qf[s] = ld_frag16(Q + off);
-      const u32x4 dou = *reinterpret_cast<const u32x4*>(dO + off);
-      const u32x4 ou = *reinterpret_cast<const u32x4*>(O + off);
-      df[s] = __builtin_bit_cast(bf16x8, dou);
+    for (int s = 0; s < DS; ++s) {
+      if (qi < pb.Tq) {
+        const int off = 16 * s + 8 * g;
+        qf[s] = ld_frag16(qr + off);
+        const u32x4 dou = *reinterpret_cast<const u32x4*>(dr + off);
+        const u32x4 ou = *reinterpret_cast<const u32x4*>(orr + off);
+        df[s] = __builtin_bit_cast(bf16x8, dou);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        dpart += bf16_lo(dou[j]) * bf16_lo(ou[j]) + bf16_hi(dou[j]) * bf16_hi(ou[j]);
-    } else {
-      qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      df[s] = qf[s];
+        for (int j = 0; j < 4; ++j)
+          dpart += bf16_lo(dou[j]) * bf16_lo(ou[j]) + bf16_hi(dou[j]) * bf16_hi(ou[j]);
+      } else {
+        qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        df[s] = qf[s];
+      }
     }
   }
   const float delta = half_sum(dpart);
-  const float nl = qi < T ? -LSE[(size_t)n * T + qi] * kLog2e : 0.0f;
-  if (qi < T && g == 0) Delta[(size_t)n * T + qi] = delta;
+  const float lse = qi < pb.Tq ? LSE[row] : -INFINITY;
+  const float nl = lse > -INFINITY ? -lse * kLog2e : -INFINITY;
+  if (qi < pb.Tq && g == 0) Delta[row] = delta;
   f32x16 nd;
 #pragma unroll
   for (int r = 0; r < 16; ++r) nd[r] = -delta;
 
-  const int kend = min(q0 + BM, T);
-  const int nkt = (kend - 1) / BN + 1;
-  const int wnkt = q0w < T ? (min(q0w + 32, T) - 1) / BN + 1 : 0;
+  const TileSpan ws = key_tiles(q0, q0 + BM - 1, pb, BN);
+  const TileSpan wv = key_tiles(q0w, q0w + 31, pb, BN);
+  const int wlast = min(q0w + 31, pb.Tq - 1);
+  const Span seen = keys_of(qi, pb);  // keys this lane's query sees
 
   RowStage<BN, D, kThreads> ks, vs;
-  ks.init(tid, LD);
-  vs.init(tid, LD);
-  ks.load(Kh, T);
-  vs.load(Vh, T);
-  ks.store(Ks[0], LD);
-  vs.store(Vs[0], LD);
+  ks.init(tid, LD, K.st);
+  vs.init(tid, LD, V.st);
+  {  // first tile (reads nothing when the workgroup sees no key)
+    const int k1 = ws.t0 * BN;
+    const int valid = ws.t1 >= ws.t0 ? pb.Tk - k1 : 0;
+    ks.load(Kh + (long long)k1 * K.st, valid);
+    vs.load(Vh + (long long)k1 * V.st, valid);
+    ks.store(Ks[0], LD);
+    vs.store(Vs[0], LD);
+  }
   __syncthreads();
 
   f32x16 acc[DE];
 #pragma unroll
   for (int e = 0; e < DE; ++e) acc[e] = zero16();
 
-  for (int kt = 0; kt < nkt; ++kt) {
-    const int buf = kt & 1;
-    const bool more = kt + 1 < nkt;
+  for (int kt = ws.t0; kt <= ws.t1; ++kt) {
+    const int buf = (kt - ws.t0) & 1;
+    const bool more = kt < ws.t1;
     if (more) {
       const int k1 = (kt + 1) * BN;
-      ks.load(Kh + (size_t)k1 * D, T - k1);
-      vs.load(Vh + (size_t)k1 * D, T - k1);
+      ks.load(Kh + (long long)k1 * K.st, pb.Tk - k1);
+      vs.load(Vh + (long long)k1 * V.st, pb.Tk - k1);
     }
-    if (kt < wnkt) {
+    if (kt >= wv.t0 && kt <= wv.t1) {
       const int k0 = kt * BN;
-      if (k0 + BN - 1 > q0w) {
-        dq_tile<D, true>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, qi, c, g, tro, sl2, nl);
+      if (needs_mask(q0w, wlast, k0, k0 + BN - 1, pb)) {
+        dq_tile<D, true>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, seen, c, g, tro, nl, pb);
       } else {
-        dq_tile<D, false>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, qi, c, g, tro, sl2, nl);
+        dq_tile<D, false>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, seen, c, g, tro, nl, pb);
       }
     }
     if (more) {
@@ -343,15 +382,16 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void attn_bwd_dq(
     __syncthreads();
   }
 
-  if (qi < T) {
-    uint16_t* row = dQ + ((size_t)n * T + qi) * D;
+  if (qi < pb.Tq) {
+    uint16_t* out = const_cast<uint16_t*>(head_of(dQ, n, pb.H)) + (long long)qi * dQ.st;
+    const float sc = pb.scale;
 #pragma unroll
     for (int e = 0; e < DE; ++e)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        u32x2 pk = {pack_bf16x2(acc[e][4 * u] * scale, acc[e][4 * u + 1] * scale),
-                    pack_bf16x2(acc[e][4 * u + 2] * scale, acc[e][4 * u + 3] * scale)};
-        *reinterpret_cast<u32x2*>(row + 32 * e + 8 * u + 4 * g) = pk;
+        u32x2 pk = {pack_bf16x2(acc[e][4 * u] * sc, acc[e][4 * u + 1] * sc),
+                    pack_bf16x2(acc[e][4 * u + 2] * sc, acc[e][4 * u + 3] * sc)};
+        *reinterpret_cast<u32x2*>(out + 32 * e + 8 * u + 4 * g) = pk;
       }
   }
 }
@@ -369,14 +409,14 @@ __device__ __forceinline__ int stat_slot(int q) {
 }
 
 // One BM-query tile for one wave (32 keys, one per lane column c).  ls/es
-// hold -lse * log2(e) and -delta of the tile's queries, permuted by
-// stat_slot; -delta seeds the dP accumulator so that the product yields
-// dP - delta directly.
+// hold -lse * log2(e) (-inf for rows that see no key or lie past Tq) and
+// -delta of the tile's queries, permuted by stat_slot; -delta seeds the dP
+// accumulator so that the product yields dP - delta directly.
 template <int D, int BM, bool MASK>
 __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db, const float* ls,
                                           const float* es, const bf16x8* kf, const bf16x8* vf,
-                                          f32x16* dvt, f32x16* dkt, int q0, int kj, int g,
-                                          int c, int tro, float sl2) {
+                                          f32x16* dvt, f32x16* dkt, int q0, Span seers, int g,
+                                          int c, int tro, const Problem& pb) {
   constexpr int LD = D + 8, DS = D / 16, DE = D / 32, NH = BM / 32;
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
@@ -397,8 +437,8 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = 8 * t + j;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], sl2, nl[r]));
-        if (MASK && kj > q0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3)) pv = 0.0f;
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], pb.sl2, nl[r]));
+        if (MASK && !inside(q0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3), seers)) pv = 0.0f;
         p[j] = pv;
         dsv[j] = pv * dp[r];
       }
@@ -419,12 +459,9 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
 
 template <int D, int BM>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
-    const float* __restrict__ LSE, const float* __restrict__ Delta,
-    uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int N, int T,
-    float sl2, float scale, int nkb) {
-  constexpr int BN = 128;
+    View Q, View K, View V, View dO, const float* __restrict__ LSE,
+    const float* __restrict__ Delta, View dK, View dV, Problem pb) {
+  constexpr int BN = kKBN;
   constexpr int LD = D + 8;     // row-major Q / dO tiles
   constexpr int DS = D / 16;
   constexpr int DE = D / 32;
@@ -438,54 +475,65 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
   const int c = lane & 31, g = lane >> 5;
   const int tro = tr_rowoff(lane) * LD + tr_coloff(lane);
   const int bid = blockIdx.x;
-  const int kb = bid / N;  // block 0 (the most queries) first
-  const int n = bid % N;
-  const uint16_t* Qh = Q + (size_t)n * T * D;
-  const uint16_t* Dh = dO + (size_t)n * T * D;
-  const size_t rows = (size_t)n * T;
+  const int kb = bid / pb.N;  // under plain causal masking, block 0 has the most queries
+  const int n = bid % pb.N;
+  const uint16_t* Qh = head_of(Q, n, pb.H);
+  const uint16_t* Dh = head_of(dO, n, pb.H);
+  const long long rows = (long long)n * pb.Tq;
   const int k0 = kb * BN;
   const int k0w = k0 + 32 * w;
   const int kj = k0w + c;
 
   bf16x8 kf[DS], vf[DS];
+  {
+    const uint16_t* kr = head_of(K, n, pb.H) + (long long)kj * K.st;
+    const uint16_t* vr = head_of(V, n, pb.H) + (long long)kj * V.st;
 #pragma unroll
-  for (int s = 0; s < DS; ++s) {
-    if (kj < T) {
-      const size_t off = (rows + kj) * D + 16 * s + 8 * g;
-      kf[s] = ld_frag16(K + off);
-      vf[s] = ld_frag16(V + off);
-    } else {
-      kf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      vf[s] = kf[s];
+    for (int s = 0; s < DS; ++s) {
+      if (kj < pb.Tk) {
+        kf[s] = ld_frag16(kr + 16 * s + 8 * g);
+        vf[s] = ld_frag16(vr + 16 * s + 8 * g);
+      } else {
+        kf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        vf[s] = kf[s];
+      }
     }
   }
 
-  const int qt0 = k0 / BM;
-  const int nqt = (T + BM - 1) / BM;
+  // query tiles that see the workgroup's keys; queries that see this wave's
+  const int qlo = queries_lo(k0, pb), qhi = queries_hi(min(k0 + BN, pb.Tk) - 1, pb);
+  const int qt0 = qlo / BM, qt1 = qhi >= qlo ? qhi / BM : qt0 - 1;
+  const int wqlo = queries_lo(k0w, pb);
+  const int wqhi = k0w < pb.Tk ? queries_hi(min(k0w + 31, pb.Tk - 1), pb) : -1;
+  const Span seers = queries_of(kj, pb);  // queries that see this lane's key
 
   RowStage<BM, D, kThreads> qs, ds;
-  qs.init(tid, LD);
-  ds.init(tid, LD);
-  float lv = 0.0f, ev = 0.0f;
-  auto load_tile = [&](int qt) {
+  qs.init(tid, LD, Q.st);
+  ds.init(tid, LD, dO.st);
+  // Row statistics of the tile: thread t < BM loads query q1 + t.  The loads
+  // only issue here; they are turned into -lse * log2(e) and -delta when the
+  // tile is stored, so that the compute in between does not wait for them.
+  float lraw = 0.0f, draw = 0.0f;
+  int qrow = 0;
+  auto load_tile = [&](int qt, int valid) {
     const int q1 = qt * BM;
-    qs.load(Qh + (size_t)q1 * D, T - q1);
-    ds.load(Dh + (size_t)q1 * D, T - q1);
-    if (tid < BM) {
-      const int q = q1 + tid;
-      lv = q < T ? -LSE[rows + q] * kLog2e : -INFINITY;
-      ev = q < T ? -Delta[rows + q] : 0.0f;
-    }
+    qs.load(Qh + (long long)q1 * Q.st, valid);
+    ds.load(Dh + (long long)q1 * dO.st, valid);
+    qrow = q1 + tid;
+    const int cnt = valid < BM ? valid : BM;  // threads tid >= BM read past it: zero
+    lraw = load_f32_or_zero(LSE + rows + q1, cnt, tid);
+    draw = load_f32_or_zero(Delta + rows + q1, cnt, tid);
   };
   auto store_tile = [&](int b) {
     qs.store(Qs[b], LD);
     ds.store(Ds[b], LD);
     if (tid < BM) {
-      Ls[b][stat_slot(tid)] = lv;
-      Es[b][stat_slot(tid)] = ev;
+      const bool live = qrow < pb.Tq && lraw > -INFINITY;  // rows past Tq or seeing no key
+      Ls[b][stat_slot(tid)] = live ? -lraw * kLog2e : -INFINITY;
+      Es[b][stat_slot(tid)] = -draw;
     }
   };
-  load_tile(qt0);
+  load_tile(qt0, qt1 >= qt0 ? pb.Tq - qt0 * BM : 0);
   store_tile(0);
   __syncthreads();
 
@@ -496,34 +544,35 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
     dkt[e] = zero16();
   }
 
-  for (int qt = qt0; qt < nqt; ++qt) {
+  for (int qt = qt0; qt <= qt1; ++qt) {
     const int buf = (qt - qt0) & 1;
-    const bool more = qt + 1 < nqt;
-    if (more) load_tile(qt + 1);
+    const bool more = qt < qt1;
+    if (more) load_tile(qt + 1, pb.Tq - (qt + 1) * BM);
     const int q0 = qt * BM;
-    if (q0 + BM - 1 >= k0w && k0w < T) {  // some query of the tile sees a key of this wave
-      if (k0w + 31 > q0) {
-        dkdv_tile<D, BM, true>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0, kj, g, c,
-                               tro, sl2);
+    if (q0 + BM - 1 >= wqlo && q0 <= wqhi) {  // some query of the tile sees a key of this wave
+      if (needs_mask(q0, q0 + BM - 1, k0w, k0w + 31, pb)) {
+        dkdv_tile<D, BM, true>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0, seers, g,
+                               c, tro, pb);
       } else {
-        dkdv_tile<D, BM, false>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0, kj, g,
-                                c, tro, sl2);
+        dkdv_tile<D, BM, false>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0, seers, g,
+                                c, tro, pb);
       }
     }
     if (more) store_tile(buf ^ 1);
     __syncthreads();
   }
 
-  if (kj < T) {
-    uint16_t* krow = dK + (rows + kj) * D;
-    uint16_t* vrow = dV + (rows + kj) * D;
+  if (kj < pb.Tk) {
+    uint16_t* krow = const_cast<uint16_t*>(head_of(dK, n, pb.H)) + (long long)kj * dK.st;
+    uint16_t* vrow = const_cast<uint16_t*>(head_of(dV, n, pb.H)) + (long long)kj * dV.st;
+    const float sc = pb.scale;
 #pragma unroll
     for (int e = 0; e < DE; ++e)
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int d = 32 * e + 8 * u + 4 * g;
-        u32x2 pk = {pack_bf16x2(dkt[e][4 * u] * scale, dkt[e][4 * u + 1] * scale),
-                    pack_bf16x2(dkt[e][4 * u + 2] * scale, dkt[e][4 * u + 3] * scale)};
+        u32x2 pk = {pack_bf16x2(dkt[e][4 * u] * sc, dkt[e][4 * u + 1] * sc),
+                    pack_bf16x2(dkt[e][4 * u + 2] * sc, dkt[e][4 * u + 3] * sc)};
         *reinterpret_cast<u32x2*>(krow + d) = pk;
         u32x2 pv = {pack_bf16x2(dvt[e][4 * u], dvt[e][4 * u + 1]),
                     pack_bf16x2(dvt[e][4 * u + 2], dvt[e][4 * u + 3])};
@@ -533,67 +582,70 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
 }
 
 template <typename... Args>
-hipError_t launch(void (*kern)(Args...), int blocks, hipStream_t stream, Args... args) {
+hipError_t launch(void (*kern)(Args...), long long blocks, hipStream_t stream, Args... args) {
   void* argv[] = {static_cast<void*>(&args)...};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3(blocks), dim3(kThreads), argv, 0,
-                         stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3((unsigned)blocks),
+                         dim3(kThreads), argv, 0, stream);
 }
 
-template <int D>
-hipError_t fwd_d(const void* q, const void* k, const void* v, void* o, float* lse, int N, int T,
-                 float scale, hipStream_t stream) {
-  const int nqb = (T + 127) / 128;
-  return launch(attn_fwd<D>, N * nqb, stream, (const uint16_t*)q, (const uint16_t*)k,
-                (const uint16_t*)v, (uint16_t*)o, lse, N, T, scale * kLog2e, nqb);
+View view(const TensorArg& t) {
+  return View{static_cast<const uint16_t*>(t.data), t.sb, t.sh, t.st};
 }
 
-template <int D>
-hipError_t bwd_dq_d(const void* q, const void* k, const void* v, const void* o, const void* dO,
-                    const float* lse, void* dq, float* delta, int N, int T, float scale,
-                    hipStream_t stream) {
-  const int nqb = (T + 127) / 128;
-  return launch(attn_bwd_dq<D>, N * nqb, stream, (const uint16_t*)q, (const uint16_t*)k,
-                (const uint16_t*)v, (const uint16_t*)o, (const uint16_t*)dO, lse, (uint16_t*)dq,
-                delta, N, T, scale * kLog2e, scale, nqb);
-}
-
-template <int D, int BM>
-hipError_t bwd_dkdv_d(const void* q, const void* k, const void* v, const void* dO,
-                      const float* lse, const float* delta, void* dk, void* dv, int N, int T,
-                      float scale, hipStream_t stream) {
-  const int nkb = (T + 127) / 128;
-  return launch(attn_bwd_dkdv<D, BM>, N * nkb, stream, (const uint16_t*)q, (const uint16_t*)k,
-                (const uint16_t*)v, (const uint16_t*)dO, lse, delta, (uint16_t*)dk,
-                (uint16_t*)dv, N, T, scale * kLog2e, scale, nkb);
+Problem problem(const ProblemArg& p) {
+  return Problem{p.B * p.H, p.H, p.Tq, p.Tk, p.off, p.win, p.scale * kLog2e, p.scale};
 }
 
 }  // namespace
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int N, int T, int D, float scale, hipStream_t stream) {
-  switch (D) {
-    case 64: return fwd_d<64>(q, k, v, o, lse, N, T, scale, stream);
-    case 128: return fwd_d<128>(q, k, v, o, lse, N, T, scale, stream);
+hipError_t launch_fwd_bf16(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                           const TensorArg& o, float* lse, const ProblemArg& p,
+                           hipStream_t stream) {
+  const Problem pb = problem(p);
+  const int nqb = (p.Tq + kBM - 1) / kBM;
+  const long long blocks = (long long)pb.N * nqb;
+  switch (p.D) {
+    case 64:
+      return launch(attn_fwd<64>, blocks, stream, view(q), view(k), view(v), view(o), lse, pb,
+                    nqb);
+    case 128:
+      return launch(attn_fwd<128>, blocks, stream, view(q), view(k), view(v), view(o), lse, pb,
+                    nqb);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o,
-                              const void* dO, const float* lse, void* dq, float* delta, int N,
-                              int T, int D, float scale, hipStream_t stream) {
-  switch (D) {
-    case 64: return bwd_dq_d<64>(q, k, v, o, dO, lse, dq, delta, N, T, scale, stream);
-    case 128: return bwd_dq_d<128>(q, k, v, o, dO, lse, dq, delta, N, T, scale, stream);
+hipError_t launch_bwd_dq_bf16(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                              const TensorArg& o, const TensorArg& dO, const float* lse,
+                              const TensorArg& dq, float* delta, const ProblemArg& p,
+                              hipStream_t stream) {
+  const Problem pb = problem(p);
+  const int nqb = (p.Tq + kBM - 1) / kBM;
+  const long long blocks = (long long)pb.N * nqb;
+  switch (p.D) {
+    case 64:
+      return launch(attn_bwd_dq<64>, blocks, stream, view(q), view(k), view(v), view(o),
+                    view(dO), lse, view(dq), delta, pb, nqb);
+    case 128:
+      return launch(attn_bwd_dq<128>, blocks, stream, view(q), view(k), view(v), view(o),
+                    view(dO), lse, view(dq), delta, pb, nqb);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dO,
-                                const float* lse, const float* delta, void* dk, void* dv, int N,
-                                int T, int D, float scale, hipStream_t stream) {
-  switch (D) {
-    case 64: return bwd_dkdv_d<64, 64>(q, k, v, dO, lse, delta, dk, dv, N, T, scale, stream);
-    case 128: return bwd_dkdv_d<128, 32>(q, k, v, dO, lse, delta, dk, dv, N, T, scale, stream);
+hipError_t launch_bwd_dkdv_bf16(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                                const TensorArg& dO, const float* lse, const float* delta,
+                                const TensorArg& dk, const TensorArg& dv, const ProblemArg& p,
+                                hipStream_t stream) {
+  const Problem pb = problem(p);
+  const long long blocks = (long long)pb.N * ((p.Tk + kKBN - 1) / kKBN);
+  switch (p.D) {
+    case 64:
+      return launch(attn_bwd_dkdv<64, 64>, blocks, stream, view(q), view(k), view(v), view(dO),
+                    lse, delta, view(dk), view(dv), pb);
+    case 128:
+      return launch(attn_bwd_dkdv<128, 32>, blocks, stream, view(q), view(k), view(v), view(dO),
+                    lse, delta, view(dk), view(dv), pb);
     default: return hipErrorInvalidValue;
   }
 }

@@ -15,6 +15,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <limits.h>
 #include <stdint.h>
 
 namespace gptattn {
@@ -106,13 +107,87 @@ __device__ __forceinline__ bf16x8 ld_frag_tr(const uint16_t* p, int ld) {
 }
 
 // ---------------------------------------------------------------------------
-// Global -> LDS staging of a ROWS x D bf16 tile (row-major in HBM, D
-// contiguous) into a row-major LDS tile with leading dimension ld.  Thread t
-// of NT moves 16-byte chunks t, t + NT, ...; eight consecutive threads cover
-// one 128-byte row segment, so each wave's loads and stores are contiguous.
-// Rows at or beyond `valid` read as zero; a full tile takes the unguarded
-// path (one uniform branch per tile).
+// Problem description shared by the kernels.
+//
+// A tensor is a [B][H][T][D] view with the D elements of each row
+// contiguous: element (b, h, t, d) sits at p + b * sb + h * sh + t * st + d.
+// Query i (of Tq) sees key j (of Tk) when j <= i + off and, with win > 0,
+// j > i + off - win (a band of the win most recent positions).  The plain
+// causal case is Tq = Tk, off = 0, win = 0.
 // ---------------------------------------------------------------------------
+struct View {
+  const uint16_t* p;
+  long long sb, sh, st;
+};
+struct Problem {
+  int N, H, Tq, Tk, off, win;
+  float sl2;    // scale * log2(e)
+  float scale;
+};
+
+template <typename P>
+__device__ __forceinline__ P head_of(P p, long long sb, long long sh, int n, int H) {
+  return p + (long long)(n / H) * sb + (long long)(n % H) * sh;
+}
+__device__ __forceinline__ const uint16_t* head_of(const View& v, int n, int H) {
+  return head_of(v.p, v.sb, v.sh, n, H);
+}
+
+// Keys query i sees, as a closed interval (empty when hi < lo), and the
+// queries that see key j (to be cut at Tq by the caller).
+struct Span {
+  int lo, hi;
+};
+__device__ __forceinline__ Span keys_of(int i, const Problem& pb) {
+  return Span{pb.win > 0 ? i + pb.off - pb.win + 1 : INT_MIN, min(i + pb.off, pb.Tk - 1)};
+}
+__device__ __forceinline__ Span queries_of(int j, const Problem& pb) {
+  return Span{j - pb.off, pb.win > 0 ? j - pb.off + pb.win - 1 : INT_MAX};
+}
+__device__ __forceinline__ bool inside(int x, Span s) { return x >= s.lo && x <= s.hi; }
+// First / last key visible to some query in [i0, i1] (clamped to the keys
+// that exist; lo > hi means none).
+__device__ __forceinline__ int keys_lo(int i0, const Problem& pb) {
+  return pb.win > 0 ? max(0, i0 + pb.off - pb.win + 1) : 0;
+}
+__device__ __forceinline__ int keys_hi(int i1, const Problem& pb) {
+  return min(pb.Tk - 1, i1 + pb.off);
+}
+// First / last query that sees some key in [j0, j1].
+__device__ __forceinline__ int queries_lo(int j0, const Problem& pb) {
+  return max(0, j0 - pb.off);
+}
+__device__ __forceinline__ int queries_hi(int j1, const Problem& pb) {
+  return pb.win > 0 ? min(pb.Tq - 1, j1 - pb.off + pb.win - 1) : pb.Tq - 1;
+}
+
+// ---------------------------------------------------------------------------
+// Global -> LDS staging of a ROWS x D bf16 tile (rows `st` elements apart in
+// HBM, st >= D, D contiguous) into a row-major LDS tile with leading
+// dimension ld.  Thread t of NT moves 16-byte chunks t, t + NT, ...; eight
+// consecutive threads cover one 128-byte row segment, so each wave's loads
+// and stores are contiguous.
+//
+// The loads are buffer loads through a descriptor whose range ends at the
+// last row that exists: the hardware returns zero for the chunks of rows at
+// or past `valid`, so a ragged last tile needs no branch and no select, and
+// the loads of a tile issue back to back.  Because st >= D, every chunk of
+// a row r < valid lies below valid * st elements and every chunk of a row
+// r >= valid lies at or above it.
+// ---------------------------------------------------------------------------
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer access (gfx9 family)
+
+// One float per thread from a range-checked buffer: element i of base[0, n)
+// (0.0f for i >= n or n <= 0, with no memory access).  base and n are
+// uniform across the workgroup; readfirstlane states that for the record
+// count, which keeps the descriptor in scalar registers.
+__device__ __forceinline__ float load_f32_or_zero(const float* base, int n, int i) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(base), 0, __builtin_amdgcn_readfirstlane(n <= 0 ? 0 : n * 4),
+      kBufferWord3);
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, i * 4, 0, 0));
+}
+
 template <int ROWS, int D, int NT>
 struct RowStage {
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
@@ -120,33 +195,30 @@ struct RowStage {
   static constexpr int RSTEP = NT / CPR;       // rows between a thread's chunks
   static_assert((ROWS * CPR) % NT == 0 && NT % CPR == 0, "tile must split evenly");
   u32x4 r[PER];
-  uint32_t goff;  // byte offset of the thread's first chunk in the global tile
-  uint32_t loff;  // element offset of the thread's first chunk in the LDS tile
-  int row;        // row of the thread's first chunk
+  uint32_t goff;   // byte offset of the thread's first chunk in the global tile
+  uint32_t gstep;  // bytes between the thread's chunks (uniform: a scalar offset)
+  uint32_t rowb;   // bytes between rows in the global tile
+  uint32_t loff;   // element offset of the thread's first chunk in the LDS tile
 
-  __device__ __forceinline__ void init(int tid, int ld) {
-    row = tid / CPR;
-    goff = (uint32_t)(row * D + 8 * (tid % CPR)) * 2u;
+  __device__ __forceinline__ void init(int tid, int ld, long long st) {
+    const int row = tid / CPR;
+    rowb = (uint32_t)(st * 2);
+    goff = (uint32_t)row * rowb + 16u * (uint32_t)(tid % CPR);
+    gstep = (uint32_t)RSTEP * rowb;
     loff = (uint32_t)(row * ld + 8 * (tid % CPR));
   }
 
-  // src: first element of the tile (uniform across the workgroup).
+  // src: first element of the tile (uniform across the workgroup); rows at or
+  // past `valid` read as zero, and with valid <= 0 nothing is read at all.
   __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int valid) {
-    const char* base = reinterpret_cast<const char*>(src) + goff;
-    if (valid >= ROWS) {
+    const int rows = valid <= 0 ? 0 : valid < ROWS ? valid : ROWS;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(src), 0, __builtin_amdgcn_readfirstlane(rows * (int)rowb),
+        kBufferWord3);
 #pragma unroll
-      for (int p = 0; p < PER; ++p)
-        r[p] = *reinterpret_cast<const u32x4*>(base + p * RSTEP * D * 2);
-      return;
-    }
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      if (row + p * RSTEP < valid) {
-        r[p] = *reinterpret_cast<const u32x4*>(base + p * RSTEP * D * 2);
-      } else {
-        r[p] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
+    for (int p = 0; p < PER; ++p)
+      r[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                           rs, (int)goff, (int)(p * gstep), 0));
   }
 
   __device__ __forceinline__ void store(uint16_t* dst, int ld) const {

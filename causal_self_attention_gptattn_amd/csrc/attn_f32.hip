@@ -7,7 +7,9 @@
 // This path exists for workloads that need float32 results (small heads,
 // tight tolerances); it runs on the vector ALUs, one lane per query (forward
 // and dQ) or per key (dK/dV), with 64-row tiles of the other operand staged
-// in LDS and shared by the wave.  Nothing is rounded below float32.
+// in LDS and shared by the wave.  Nothing is rounded below float32.  Each
+// lane walks exactly the keys (or queries) its row can see under the
+// visibility rule of attn_common.h.
 #include "attn_common.h"
 #include "launch.h"
 
@@ -17,54 +19,71 @@ namespace {
 
 constexpr int kRows = 64;  // lanes per workgroup and rows per staged tile
 
-// Stage rows [r0, r0 + 64) of an [T][D] float matrix into LDS (zero past T).
+struct FView {
+  const float* p;
+  long long sb, sh, st;
+};
+
+__device__ __forceinline__ const float* head_of(const FView& v, int n, int H) {
+  return gptattn::head_of(v.p, v.sb, v.sh, n, H);
+}
+
+// Stage rows [r0, r0 + 64) of one head (rows st floats apart, D contiguous)
+// into a dense [64][D] LDS tile; rows at or past `rows` read as zero.
 template <int D>
-__device__ __forceinline__ void stage_rows(float* dst, const float* __restrict__ src, int r0, int T,
-                                           int tid) {
+__device__ __forceinline__ void stage_rows(float* dst, const float* __restrict__ src,
+                                           long long st, int r0, int rows, int tid) {
   constexpr int F4 = D / 4;
   for (int i = tid; i < kRows * F4; i += kRows) {
     const int row = i / F4, col = i % F4;
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (r0 + row < T) v = *reinterpret_cast<const f32x4*>(src + (size_t)(r0 + row) * D + 4 * col);
+    if (r0 + row < rows)
+      v = *reinterpret_cast<const f32x4*>(src + (long long)(r0 + row) * st + 4 * col);
     *reinterpret_cast<f32x4*>(dst + row * D + 4 * col) = v;
   }
 }
 
+// Keys query i sees: [lo, hi] (empty when hi < lo or i is past Tq).
+__device__ __forceinline__ void key_range(int i, const Problem& pb, int& lo, int& hi) {
+  lo = keys_lo(i, pb);
+  hi = i < pb.Tq ? keys_hi(i, pb) : -1;
+}
+
 template <int D>
-__global__ __launch_bounds__(kRows) void attn_fwd_f32(const float* __restrict__ Q,
-                                                      const float* __restrict__ K,
-                                                      const float* __restrict__ V,
-                                                      float* __restrict__ O,
-                                                      float* __restrict__ LSE, int T,
-                                                      float scale) {
+__global__ __launch_bounds__(kRows) void attn_fwd_f32(FView Q, FView K, FView V, FView O,
+                                                      float* __restrict__ LSE, Problem pb,
+                                                      int nt) {
   __shared__ __attribute__((aligned(16))) float Ks[kRows * D];
   __shared__ __attribute__((aligned(16))) float Vs[kRows * D];
   const int tid = threadIdx.x;
-  const int nt = (T + kRows - 1) / kRows;
   const int n = blockIdx.x / nt;
   const int q0 = (blockIdx.x % nt) * kRows;
   const int qi = q0 + tid;
-  const size_t head = (size_t)n * T * D;
+  const float* Kh = head_of(K, n, pb.H);
+  const float* Vh = head_of(V, n, pb.H);
+  const float* qr = head_of(Q, n, pb.H) + (long long)qi * Q.st;
   float q[D], acc[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    q[d] = qi < T ? Q[head + (size_t)qi * D + d] : 0.0f;
+    q[d] = qi < pb.Tq ? qr[d] : 0.0f;
     acc[d] = 0.0f;
   }
+  int lo, hi;
+  key_range(qi, pb, lo, hi);
   float m = -INFINITY, l = 0.0f;
-  const int kend = min(q0 + kRows, T);
-  for (int k0 = 0; k0 < kend; k0 += kRows) {
-    stage_rows<D>(Ks, K + head, k0, T, tid);
-    stage_rows<D>(Vs, V + head, k0, T, tid);
+  const int klo = keys_lo(q0, pb), khi = keys_hi(min(q0 + kRows, pb.Tq) - 1, pb);
+  for (int k0 = klo / kRows * kRows; k0 <= khi; k0 += kRows) {
+    stage_rows<D>(Ks, Kh, K.st, k0, pb.Tk, tid);
+    stage_rows<D>(Vs, Vh, V.st, k0, pb.Tk, tid);
     __syncthreads();
-    const int jmax = min(kRows, qi - k0 + 1);  // keys k0 + j <= qi
-    for (int j = 0; j < jmax; ++j) {
+    const int j0 = max(0, lo - k0), j1 = min(kRows - 1, hi - k0);
+    for (int j = j0; j <= j1; ++j) {
       float s = 0.0f;
 #pragma unroll
       for (int d = 0; d < D; ++d) s = __builtin_fmaf(q[d], Ks[j * D + d], s);
-      s *= scale;
+      s *= pb.scale;
       if (s > m) {
-        const float corr = expf(m - s);
+        const float corr = expf(m - s);  // 0 for the first key (m = -inf)
         l = l * corr + 1.0f;
 #pragma unroll
         for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(acc[d], corr, Vs[j * D + d]);
@@ -78,107 +97,124 @@ __global__ __launch_bounds__(kRows) void attn_fwd_f32(const float* __restrict__ 
     }
     __syncthreads();
   }
-  if (qi < T) {
-    const float inv = 1.0f / l;
+  if (qi < pb.Tq) {
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;  // a row that sees no key outputs 0
+    float* orow = const_cast<float*>(head_of(O, n, pb.H)) + (long long)qi * O.st;
 #pragma unroll
-    for (int d = 0; d < D; ++d) O[head + (size_t)qi * D + d] = acc[d] * inv;
-    LSE[(size_t)n * T + qi] = m + logf(l);
+    for (int d = 0; d < D; ++d) orow[d] = acc[d] * inv;
+    LSE[(long long)n * pb.Tq + qi] = l > 0.0f ? m + logf(l) : -INFINITY;
   }
 }
 
-// delta_i = sum_d dO_id O_id, then dQ_i = scale sum_{j<=i} P_ij (dP_ij - delta_i) K_j
+// delta_i = sum_d dO_id O_id, then dQ_i = scale sum_j P_ij (dP_ij - delta_i) K_j
+// over the keys j that query i sees.
 template <int D>
-__global__ __launch_bounds__(kRows) void attn_bwd_dq_f32(
-    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    const float* __restrict__ O, const float* __restrict__ dO, const float* __restrict__ LSE,
-    float* __restrict__ dQ, float* __restrict__ Delta, int T, float scale) {
+__global__ __launch_bounds__(kRows) void attn_bwd_dq_f32(FView Q, FView K, FView V, FView O,
+                                                         FView dO, const float* __restrict__ LSE,
+                                                         FView dQ, float* __restrict__ Delta,
+                                                         Problem pb, int nt) {
   __shared__ __attribute__((aligned(16))) float Ks[kRows * D];
   __shared__ __attribute__((aligned(16))) float Vs[kRows * D];
   const int tid = threadIdx.x;
-  const int nt = (T + kRows - 1) / kRows;
   const int n = blockIdx.x / nt;
   const int q0 = (blockIdx.x % nt) * kRows;
   const int qi = q0 + tid;
-  const size_t head = (size_t)n * T * D;
+  const float* Kh = head_of(K, n, pb.H);
+  const float* Vh = head_of(V, n, pb.H);
+  const float* qr = head_of(Q, n, pb.H) + (long long)qi * Q.st;
+  const float* gr = head_of(dO, n, pb.H) + (long long)qi * dO.st;
+  const float* orr = head_of(O, n, pb.H) + (long long)qi * O.st;
+  const bool live = qi < pb.Tq;
   float q[D], g[D], acc[D];
   float delta = 0.0f;
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    const size_t off = head + (size_t)qi * D + d;
-    q[d] = qi < T ? Q[off] : 0.0f;
-    g[d] = qi < T ? dO[off] : 0.0f;
-    delta = __builtin_fmaf(g[d], qi < T ? O[off] : 0.0f, delta);
+    q[d] = live ? qr[d] : 0.0f;
+    g[d] = live ? gr[d] : 0.0f;
+    delta = __builtin_fmaf(g[d], live ? orr[d] : 0.0f, delta);
     acc[d] = 0.0f;
   }
-  const float lse = qi < T ? LSE[(size_t)n * T + qi] : 0.0f;
-  if (qi < T) Delta[(size_t)n * T + qi] = delta;
-  const int kend = min(q0 + kRows, T);
-  for (int k0 = 0; k0 < kend; k0 += kRows) {
-    stage_rows<D>(Ks, K + head, k0, T, tid);
-    stage_rows<D>(Vs, V + head, k0, T, tid);
+  const long long row = (long long)n * pb.Tq + qi;
+  const float lse = live ? LSE[row] : 0.0f;
+  if (live) Delta[row] = delta;
+  int lo, hi;
+  key_range(qi, pb, lo, hi);
+  const int klo = keys_lo(q0, pb), khi = keys_hi(min(q0 + kRows, pb.Tq) - 1, pb);
+  for (int k0 = klo / kRows * kRows; k0 <= khi; k0 += kRows) {
+    stage_rows<D>(Ks, Kh, K.st, k0, pb.Tk, tid);
+    stage_rows<D>(Vs, Vh, V.st, k0, pb.Tk, tid);
     __syncthreads();
-    const int jmax = min(kRows, qi - k0 + 1);
-    for (int j = 0; j < jmax; ++j) {
+    const int j0 = max(0, lo - k0), j1 = min(kRows - 1, hi - k0);
+    for (int j = j0; j <= j1; ++j) {
       float s = 0.0f, dp = 0.0f;
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         s = __builtin_fmaf(q[d], Ks[j * D + d], s);
         dp = __builtin_fmaf(g[d], Vs[j * D + d], dp);
       }
-      const float p = expf(s * scale - lse);
+      const float p = expf(s * pb.scale - lse);
       const float ds = p * (dp - delta);
 #pragma unroll
       for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(ds, Ks[j * D + d], acc[d]);
     }
     __syncthreads();
   }
-  if (qi < T) {
+  if (live) {
+    float* out = const_cast<float*>(head_of(dQ, n, pb.H)) + (long long)qi * dQ.st;
 #pragma unroll
-    for (int d = 0; d < D; ++d) dQ[head + (size_t)qi * D + d] = acc[d] * scale;
+    for (int d = 0; d < D; ++d) out[d] = acc[d] * pb.scale;
   }
 }
 
-// dV_j = sum_{i>=j} P_ij dO_i,  dK_j = scale sum_{i>=j} P_ij (dP_ij - delta_i) Q_i
+// dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i P_ij (dP_ij - delta_i) Q_i over
+// the queries i that see key j.
 template <int D>
-__global__ __launch_bounds__(kRows) void attn_bwd_dkdv_f32(
-    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    const float* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Delta,
-    float* __restrict__ dK, float* __restrict__ dV, int T, float scale) {
+__global__ __launch_bounds__(kRows) void attn_bwd_dkdv_f32(FView Q, FView K, FView V, FView dO,
+                                                           const float* __restrict__ LSE,
+                                                           const float* __restrict__ Delta,
+                                                           FView dK, FView dV, Problem pb,
+                                                           int nt) {
   __shared__ __attribute__((aligned(16))) float Qs[kRows * D];
   __shared__ __attribute__((aligned(16))) float Gs[kRows * D];
   __shared__ float Ls[kRows], Es[kRows];
   const int tid = threadIdx.x;
-  const int nt = (T + kRows - 1) / kRows;
   const int n = blockIdx.x / nt;
   const int k0 = (blockIdx.x % nt) * kRows;
   const int kj = k0 + tid;
-  const size_t head = (size_t)n * T * D;
+  const float* Qh = head_of(Q, n, pb.H);
+  const float* Gh = head_of(dO, n, pb.H);
+  const float* kr = head_of(K, n, pb.H) + (long long)kj * K.st;
+  const float* vr = head_of(V, n, pb.H) + (long long)kj * V.st;
+  const long long rows = (long long)n * pb.Tq;
+  const bool live = kj < pb.Tk;
   float k[D], v[D], dk[D], dv[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    const size_t off = head + (size_t)kj * D + d;
-    k[d] = kj < T ? K[off] : 0.0f;
-    v[d] = kj < T ? V[off] : 0.0f;
+    k[d] = live ? kr[d] : 0.0f;
+    v[d] = live ? vr[d] : 0.0f;
     dk[d] = 0.0f;
     dv[d] = 0.0f;
   }
-  for (int q0 = k0; q0 < T; q0 += kRows) {
-    stage_rows<D>(Qs, Q + head, q0, T, tid);
-    stage_rows<D>(Gs, dO + head, q0, T, tid);
+  // queries that see key kj: [lo, hi]
+  const int lo = queries_lo(kj, pb);
+  const int hi = live ? queries_hi(kj, pb) : -1;
+  const int qlo = queries_lo(k0, pb), qhi = queries_hi(min(k0 + kRows, pb.Tk) - 1, pb);
+  for (int q0 = qlo / kRows * kRows; q0 <= qhi; q0 += kRows) {
+    stage_rows<D>(Qs, Qh, Q.st, q0, pb.Tq, tid);
+    stage_rows<D>(Gs, Gh, dO.st, q0, pb.Tq, tid);
     const int qt = q0 + tid;
-    Ls[tid] = qt < T ? LSE[(size_t)n * T + qt] : 0.0f;
-    Es[tid] = qt < T ? Delta[(size_t)n * T + qt] : 0.0f;
+    Ls[tid] = qt < pb.Tq ? LSE[rows + qt] : 0.0f;
+    Es[tid] = qt < pb.Tq ? Delta[rows + qt] : 0.0f;
     __syncthreads();
-    const int imin = max(0, kj - q0);        // queries q0 + i >= kj
-    const int imax = min(kRows, T - q0);
-    for (int i = imin; i < imax; ++i) {
+    const int i0 = max(0, lo - q0), i1 = min(kRows - 1, hi - q0);
+    for (int i = i0; i <= i1; ++i) {
       float s = 0.0f, dp = 0.0f;
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         s = __builtin_fmaf(Qs[i * D + d], k[d], s);
         dp = __builtin_fmaf(Gs[i * D + d], v[d], dp);
       }
-      const float p = expf(s * scale - Ls[i]);
+      const float p = expf(s * pb.scale - Ls[i]);
       const float ds = p * (dp - Es[i]);
 #pragma unroll
       for (int d = 0; d < D; ++d) {
@@ -188,74 +224,92 @@ __global__ __launch_bounds__(kRows) void attn_bwd_dkdv_f32(
     }
     __syncthreads();
   }
-  if (kj < T) {
+  if (live) {
+    float* kw = const_cast<float*>(head_of(dK, n, pb.H)) + (long long)kj * dK.st;
+    float* vw = const_cast<float*>(head_of(dV, n, pb.H)) + (long long)kj * dV.st;
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      dK[head + (size_t)kj * D + d] = dk[d] * scale;
-      dV[head + (size_t)kj * D + d] = dv[d];
+      kw[d] = dk[d] * pb.scale;
+      vw[d] = dv[d];
     }
   }
 }
 
 template <typename... Args>
-hipError_t launch(void (*kern)(Args...), dim3 grid, hipStream_t stream, Args... args) {
+hipError_t launch(void (*kern)(Args...), long long blocks, hipStream_t stream, Args... args) {
   void* argv[] = {static_cast<void*>(&args)...};
-  return hipLaunchKernel(reinterpret_cast<const void*>(kern), grid, dim3(kRows), argv, 0, stream);
+  return hipLaunchKernel(reinterpret_cast<const void*>(kern), dim3((unsigned)blocks),
+                         dim3(kRows), argv, 0, stream);
+}
+
+FView view(const TensorArg& t) {
+  return FView{static_cast<const float*>(t.data), t.sb, t.sh, t.st};
+}
+
+Problem problem(const ProblemArg& p) {
+  return Problem{p.B * p.H, p.H, p.Tq, p.Tk, p.off, p.win, p.scale * kLog2e, p.scale};
 }
 
 template <int D>
-hipError_t fwd_d(const float* q, const float* k, const float* v, float* o, float* lse, int N,
-                 int T, float scale, hipStream_t stream) {
-  const dim3 grid(N * ((T + kRows - 1) / kRows));
-  return launch(attn_fwd_f32<D>, grid, stream, q, k, v, o, lse, T, scale);
+hipError_t fwd_d(const TensorArg& q, const TensorArg& k, const TensorArg& v, const TensorArg& o,
+                 float* lse, const ProblemArg& p, hipStream_t stream) {
+  const int nt = (p.Tq + kRows - 1) / kRows;
+  return launch(attn_fwd_f32<D>, (long long)p.B * p.H * nt, stream, view(q), view(k), view(v),
+                view(o), lse, problem(p), nt);
 }
 
 template <int D>
-hipError_t bwd_dq_d(const float* q, const float* k, const float* v, const float* o,
-                    const float* dO, const float* lse, float* dq, float* delta, int N, int T,
-                    float scale, hipStream_t stream) {
-  const dim3 grid(N * ((T + kRows - 1) / kRows));
-  return launch(attn_bwd_dq_f32<D>, grid, stream, q, k, v, o, dO, lse, dq, delta, T, scale);
+hipError_t bwd_dq_d(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                    const TensorArg& o, const TensorArg& dO, const float* lse,
+                    const TensorArg& dq, float* delta, const ProblemArg& p, hipStream_t stream) {
+  const int nt = (p.Tq + kRows - 1) / kRows;
+  return launch(attn_bwd_dq_f32<D>, (long long)p.B * p.H * nt, stream, view(q), view(k),
+                view(v), view(o), view(dO), lse, view(dq), delta, problem(p), nt);
 }
 
 template <int D>
-hipError_t bwd_dkdv_d(const float* q, const float* k, const float* v, const float* dO,
-                      const float* lse, const float* delta, float* dk, float* dv, int N, int T,
-                      float scale, hipStream_t stream) {
-  const dim3 grid(N * ((T + kRows - 1) / kRows));
-  return launch(attn_bwd_dkdv_f32<D>, grid, stream, q, k, v, dO, lse, delta, dk, dv, T, scale);
+hipError_t bwd_dkdv_d(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                      const TensorArg& dO, const float* lse, const float* delta,
+                      const TensorArg& dk, const TensorArg& dv, const ProblemArg& p,
+                      hipStream_t stream) {
+  const int nt = (p.Tk + kRows - 1) / kRows;
+  return launch(attn_bwd_dkdv_f32<D>, (long long)p.B * p.H * nt, stream, view(q), view(k),
+                view(v), view(dO), lse, delta, view(dk), view(dv), problem(p), nt);
 }
 
 }  // namespace
 
-hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int N, int T, int D, float scale, hipStream_t stream) {
-  switch (D) {
-    case 16: return fwd_d<16>(q, k, v, o, lse, N, T, scale, stream);
-    case 32: return fwd_d<32>(q, k, v, o, lse, N, T, scale, stream);
-    case 64: return fwd_d<64>(q, k, v, o, lse, N, T, scale, stream);
+hipError_t launch_fwd_f32(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                          const TensorArg& o, float* lse, const ProblemArg& p,
+                          hipStream_t stream) {
+  switch (p.D) {
+    case 16: return fwd_d<16>(q, k, v, o, lse, p, stream);
+    case 32: return fwd_d<32>(q, k, v, o, lse, p, stream);
+    case 64: return fwd_d<64>(q, k, v, o, lse, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_bwd_dq_f32(const float* q, const float* k, const float* v, const float* o,
-                             const float* dO, const float* lse, float* dq, float* delta, int N,
-                             int T, int D, float scale, hipStream_t stream) {
-  switch (D) {
-    case 16: return bwd_dq_d<16>(q, k, v, o, dO, lse, dq, delta, N, T, scale, stream);
-    case 32: return bwd_dq_d<32>(q, k, v, o, dO, lse, dq, delta, N, T, scale, stream);
-    case 64: return bwd_dq_d<64>(q, k, v, o, dO, lse, dq, delta, N, T, scale, stream);
+hipError_t launch_bwd_dq_f32(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                             const TensorArg& o, const TensorArg& dO, const float* lse,
+                             const TensorArg& dq, float* delta, const ProblemArg& p,
+                             hipStream_t stream) {
+  switch (p.D) {
+    case 16: return bwd_dq_d<16>(q, k, v, o, dO, lse, dq, delta, p, stream);
+    case 32: return bwd_dq_d<32>(q, k, v, o, dO, lse, dq, delta, p, stream);
+    case 64: return bwd_dq_d<64>(q, k, v, o, dO, lse, dq, delta, p, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_bwd_dkdv_f32(const float* q, const float* k, const float* v, const float* dO,
-                               const float* lse, const float* delta, float* dk, float* dv, int N,
-                               int T, int D, float scale, hipStream_t stream) {
-  switch (D) {
-    case 16: return bwd_dkdv_d<16>(q, k, v, dO, lse, delta, dk, dv, N, T, scale, stream);
-    case 32: return bwd_dkdv_d<32>(q, k, v, dO, lse, delta, dk, dv, N, T, scale, stream);
-    case 64: return bwd_dkdv_d<64>(q, k, v, dO, lse, delta, dk, dv, N, T, scale, stream);
+hipError_t launch_bwd_dkdv_f32(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                               const TensorArg& dO, const float* lse, const float* delta,
+                               const TensorArg& dk, const TensorArg& dv, const ProblemArg& p,
+                               hipStream_t stream) {
+  switch (p.D) {
+    case 16: return bwd_dkdv_d<16>(q, k, v, dO, lse, delta, dk, dv, p, stream);
+    case 32: return bwd_dkdv_d<32>(q, k, v, dO, lse, delta, dk, dv, p, stream);
+    case 64: return bwd_dkdv_d<64>(q, k, v, dO, lse, delta, dk, dv, p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -6,26 +6,46 @@
 
 namespace gptattn {
 
-// bf16 storage, D in {64, 128}; N = B * H independent head-problems.
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int N, int T, int D, float scale, hipStream_t stream);
-// Backward in two launches.  delta: N * T floats, the row term
-// sum_d dO O, written by the dq launch and read by the dk/dv launch.
-hipError_t launch_bwd_dq_bf16(const void* q, const void* k, const void* v, const void* o,
-                              const void* dO, const float* lse, void* dq, float* delta, int N,
-                              int T, int D, float scale, hipStream_t stream);
-hipError_t launch_bwd_dkdv_bf16(const void* q, const void* k, const void* v, const void* dO,
-                                const float* lse, const float* delta, void* dk, void* dv, int N,
-                                int T, int D, float scale, hipStream_t stream);
+// A [B][H][rows][D] tensor with D contiguous: element (b, h, t, d) is at
+// data + b * sb + h * sh + t * st + d (strides in elements).
+struct TensorArg {
+  const void* data;
+  long long sb, sh, st;
+};
 
-// float32 storage, D in {16, 32, 64}.
-hipError_t launch_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
-                          int N, int T, int D, float scale, hipStream_t stream);
-hipError_t launch_bwd_dq_f32(const float* q, const float* k, const float* v, const float* o,
-                             const float* dO, const float* lse, float* dq, float* delta, int N,
-                             int T, int D, float scale, hipStream_t stream);
-hipError_t launch_bwd_dkdv_f32(const float* q, const float* k, const float* v, const float* dO,
-                               const float* lse, const float* delta, float* dk, float* dv, int N,
-                               int T, int D, float scale, hipStream_t stream);
+// Query i of Tq sees key j of Tk when j <= i + off and, with win > 0,
+// j > i + off - win.  Plain causal attention: Tq = Tk, off = 0, win = 0.
+struct ProblemArg {
+  int B, H, Tq, Tk, D, off, win;
+  float scale;
+};
+
+// bf16 storage, D in {64, 128}.  lse: [B][H][Tq] float32, contiguous.
+hipError_t launch_fwd_bf16(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                           const TensorArg& o, float* lse, const ProblemArg& p,
+                           hipStream_t stream);
+// Backward in two launches.  delta: [B][H][Tq] floats, the row term
+// sum_d dO O, written by the dq launch and read by the dk/dv launch.
+hipError_t launch_bwd_dq_bf16(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                              const TensorArg& o, const TensorArg& dO, const float* lse,
+                              const TensorArg& dq, float* delta, const ProblemArg& p,
+                              hipStream_t stream);
+hipError_t launch_bwd_dkdv_bf16(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                                const TensorArg& dO, const float* lse, const float* delta,
+                                const TensorArg& dk, const TensorArg& dv, const ProblemArg& p,
+                                hipStream_t stream);
+
+// float32 storage, D in {16, 32, 64}; same arguments.
+hipError_t launch_fwd_f32(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                          const TensorArg& o, float* lse, const ProblemArg& p,
+                          hipStream_t stream);
+hipError_t launch_bwd_dq_f32(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                             const TensorArg& o, const TensorArg& dO, const float* lse,
+                             const TensorArg& dq, float* delta, const ProblemArg& p,
+                             hipStream_t stream);
+hipError_t launch_bwd_dkdv_f32(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                               const TensorArg& dO, const float* lse, const float* delta,
+                               const TensorArg& dk, const TensorArg& dv, const ProblemArg& p,
+                               hipStream_t stream);
 
 }  // namespace gptattn

@@ -154,6 +154,93 @@ int gptattn_bwd_dkdv_f32(const float* q, const float* k, const float* v,
  */
 size_t gptattn_bwd_workspace_bytes(int B, int H, int T, int D, int is_f32);
 
+/* ------------------------------------------------------------------------
+ * Generalised calls: strided tensors, Tq != Tk, shifted and banded masks.
+ *
+ * Same operation as above with two generalisations:
+ *
+ * 1. Strided views.  Heads are a batch dimension reached by a reshape
+ *    (lecture chapters "multi-headed self-attention" and "batched
+ *    multi-headed self-attention", exercise EX1), so a tensor need not be a
+ *    dense [B][H][T][D] array: element (b, h, t, d) is read at
+ *        data + b*stride_b + h*stride_h + t*stride_t + d       (elements)
+ *    with the D elements of a row contiguous.  This reads q, k and v in
+ *    place from one packed projection output [B][T][3][H][D] (stride_b =
+ *    T*3*H*D, stride_h = D, stride_t = 3*H*D, k and v at offsets H*D and
+ *    2*H*D) and writes o straight into a [B][T][H][D] buffer.  Strides are
+ *    non-negative multiples of 16 bytes; rows do not overlap (stride_t >= D
+ *    when the view has more than one row; with one row stride_t is
+ *    ignored); stride_t is at most 2^23 elements.
+ *    An input stride may be 0 (the same keys and values for every head).
+ *    Output views must not repeat an element, and outputs must not overlap
+ *    each other or an input; overlap is tested on address ranges and, for
+ *    interleaved views such as q/k/v of one packed buffer, on their common
+ *    period.  A layout the test cannot prove disjoint is refused.
+ *
+ * 2. Visibility.  Query i (0 <= i < Tq) sees key j (0 <= j < Tk) when
+ *        j <= i + causal_offset            (nothing from its future)
+ *    and, if window > 0, also
+ *        j >  i + causal_offset - window   (only the `window` most recent)
+ *    causal_offset = Tk - Tq places Tq new queries after a context of
+ *    Tk - Tq positions (Tq = 1: one decoding step).  window > 0 gives the
+ *    locally banded causal pattern that GPT-3 alternates with dense layers
+ *    (minGPT README, GPT-3 notes).  causal_offset = 0, window = 0,
+ *    Tq = Tk is the plain causal case of gptattn_fwd.  A query that sees no
+ *    key (possible when causal_offset < 0) gets O = 0 and lse = -inf and
+ *    contributes no gradient.
+ *
+ * lse and the workspace stay dense: [B][H][Tq] float32.
+ * ------------------------------------------------------------------------ */
+
+enum gptattn_dtype {
+  GPTATTN_DTYPE_BF16 = 0, /* bfloat16 tensors, matrix cores; D in {64, 128} */
+  GPTATTN_DTYPE_F32 = 1   /* float32 tensors, all steps float32; D in {16, 32, 64} */
+};
+
+typedef struct gptattn_tensor {
+  void* data;         /* device pointer to element (0, 0, 0, 0), 16-byte aligned */
+  long long stride_b; /* elements between consecutive batch entries */
+  long long stride_h; /* elements between consecutive heads */
+  long long stride_t; /* elements between consecutive positions */
+} gptattn_tensor;
+
+typedef struct gptattn_problem {
+  int B, H;          /* batch size and heads, >= 1 */
+  int Tq, Tk;        /* query and key/value lengths, 1 .. 2^29 */
+  int D;             /* head size */
+  int causal_offset; /* -2^29 .. 2^29 */
+  int window;        /* 0 (unbounded) or band width 1 .. 2^29 */
+  float scale;       /* finite, > 0; 1/sqrt(D) for standard attention */
+  int dtype;         /* enum gptattn_dtype */
+} gptattn_problem;
+
+/*
+ * Forward pass over views.
+ *   q : Tq rows; k, v : Tk rows; read only.
+ *   o : Tq rows, written.
+ *   lse : [B][H][Tq] float32, written.
+ * Errors as for gptattn_fwd (dtype outside the enum is INVALID_VALUE).
+ */
+int gptattn_fwd_ex(const gptattn_problem* p, const gptattn_tensor* q,
+                   const gptattn_tensor* k, const gptattn_tensor* v,
+                   const gptattn_tensor* o, float* lse, void* stream);
+
+/*
+ * Backward pass over views (the two launches of gptattn_bwd, on `stream`).
+ *   q, o, dO : Tq rows; k, v : Tk rows; lse : [B][H][Tq]; read only.
+ *   dq : Tq rows; dk, dv : Tk rows; written.
+ *   workspace : at least gptattn_bwd_ex_workspace_bytes(p) bytes.
+ */
+int gptattn_bwd_ex(const gptattn_problem* p, const gptattn_tensor* q,
+                   const gptattn_tensor* k, const gptattn_tensor* v,
+                   const gptattn_tensor* o, const gptattn_tensor* dO,
+                   const float* lse, const gptattn_tensor* dq,
+                   const gptattn_tensor* dk, const gptattn_tensor* dv,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes for gptattn_bwd_ex (B*H*Tq float32); 0 if p is invalid. */
+size_t gptattn_bwd_ex_workspace_bytes(const gptattn_problem* p);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* gptattn_status_string(int status);
 

@@ -1,0 +1,166 @@
+"""GPU parity of the strided entry points (gptattn_fwd_ex / gptattn_bwd_ex)
+against the float64 oracle.
+
+* Packed layout: q, k, v read in place from one [B, T, 3C] projection output,
+  o written into a [B, T, C] buffer and dq, dk, dv into one packed gradient
+  buffer.  The kernels are the ones the dense entry points run, so the
+  result must also equal the dense path bit for bit.
+* Tq != Tk with a causal offset (new queries after a context, one decoding
+  step), rows that see no key, and banded windows (GPT-3's locally banded
+  layers, minGPT README notes), in both precisions, with ragged tails.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import causal_self_attention_gptattn_amd as G
+from causal_self_attention_gptattn_amd import workloads as W
+
+from gpu_helpers import compare, need_gpu, run_oracle, sample_heads, say, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def packed_from(inp, dev):
+    """[B, T, 3C] buffer holding q | k | v (heads in order) and its views."""
+    q, k, v = (inp[n] for n in ("q", "k", "v"))
+    B, H, T, D = q.shape
+    x = torch.cat([t.transpose(1, 2).reshape(B, T, H * D) for t in (q, k, v)], dim=-1)
+    x = x.to(dev).contiguous()
+    return x, G.split_qkv(x, H)
+
+
+def test_packed_layout_matches_oracle_and_dense_path():
+    dev = need_gpu()
+    B, H, T, D = 4, 12, 1024, 64
+    say("packed", B, H, T, D)
+    inp = W.make_inputs(B, H, T, D, "bf16", seed=5)
+    sc = inp["scale"]
+    x, (q, k, v) = packed_from(inp, dev)
+    assert q.stride() == (T * 3 * H * D, D, 3 * H * D, 1)
+    y = torch.empty(B, T, H * D, dtype=torch.bfloat16, device=dev)
+    o_view = y.view(B, T, H, D).transpose(1, 2)
+    o, lse = G.fwd_ex(q, k, v, sc, out=o_view)
+    assert o.data_ptr() == y.data_ptr()
+    do = inp["do"].to(dev)
+    gx = torch.full_like(x, float("nan"))
+    dq, dk, dv = G.split_qkv(gx, H)
+    G.bwd_ex(q, k, v, o, do, lse, sc, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert not torch.isnan(gx).any(), "packed gradient buffer not fully written"
+    got = {"o": to64(o), "lse": to64(lse), "dq": to64(dq), "dk": to64(dk), "dv": to64(dv)}
+
+    # bitwise equal to the dense entry points on contiguous copies
+    qc, kc, vc = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o2, lse2 = G.fwd(qc, kc, vc, sc)
+    g2 = G.bwd(qc, kc, vc, o2, do, lse2, sc)
+    torch.cuda.synchronize()
+    assert torch.equal(o.contiguous(), o2) and torch.equal(lse, lse2)
+    for a, b in zip((dq, dk, dv), g2):
+        assert torch.equal(a.contiguous(), b)
+
+    heads = sample_heads(B, H, 6, seed=5)
+    compare(got, run_oracle(inp, heads), "bf16", heads, label="packed")
+
+
+def test_packed_autograd():
+    dev = need_gpu()
+    B, H, T, D = 2, 4, 200, 64
+    inp = W.make_inputs(B, H, T, D, "bf16", seed=6)
+    x, _ = packed_from(inp, dev)
+    x.requires_grad_(True)
+    q, k, v = G.split_qkv(x, H)
+    o = G.attention(q, k, v, inp["scale"])
+    o.backward(inp["do"].to(dev))
+    torch.cuda.synchronize()
+    gq, gk, gv = G.split_qkv(x.grad, H)
+    got = {"o": to64(o), "lse": np.zeros((B, H, T)), "dq": to64(gq), "dk": to64(gk),
+           "dv": to64(gv)}
+    ref = run_oracle(inp)
+    ref["lse"] = np.zeros((B, H, T))
+    compare(got, ref, "bf16", label="packed autograd")
+
+
+def shifted_inputs(B, H, Tq, Tk, D, dtype, seed):
+    """Queries are the last Tq positions of a max(Tq, Tk)-long sequence and
+    keys/values its first Tk positions (the decode / appended-query shape
+    when Tq <= Tk and offset = Tk - Tq)."""
+    T = max(Tq, Tk)
+    inp = W.make_inputs(B, H, T, D, dtype, seed, "projection" if dtype == "bf16" else "iid")
+    out = dict(inp)
+    for n in ("q", "do"):
+        out[n] = inp[n][:, :, T - Tq:].contiguous()
+    for n in ("k", "v"):
+        out[n] = inp[n][:, :, :Tk].contiguous()
+    return out
+
+
+def run_ex(inp, dev, off, win):
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = G.fwd_ex(q, k, v, inp["scale"], off, win)
+    dq, dk, dv = G.bwd_ex(q, k, v, o, do, lse, inp["scale"], off, win)
+    torch.cuda.synchronize()
+    return {"o": to64(o), "lse": to64(lse), "dq": to64(dq), "dk": to64(dk), "dv": to64(dv)}
+
+
+# (B, H, Tq, Tk, offset, window)
+SHAPES = [
+    (2, 3, 1, 1024, 1023, 0),      # one decoding step over a 1024-token context
+    (2, 3, 1, 77, 76, 0),
+    (1, 4, 100, 300, 200, 0),      # 100 new queries after 200 context tokens
+    (1, 2, 129, 129, 0, 64),       # banded causal, window 64
+    (1, 2, 300, 300, 0, 1),        # window 1: each query sees only itself
+    (1, 2, 257, 257, 0, 100),
+    (1, 2, 64, 500, 436, 100),     # appended queries under a band
+    (1, 2, 200, 130, -70, 0),      # first 70 queries see no key
+    (1, 2, 150, 150, -20, 33),
+    (1, 2, 40, 500, 10, 0),        # keys far past every query stay unused
+    (1, 2, 65, 63, 5, 0),
+    (1, 2, 31, 31, 40, 0),         # offset past the end: every query sees all keys
+]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B,H,Tq,Tk,off,win", SHAPES)
+def test_shifted_and_banded_bf16(B, H, Tq, Tk, off, win, D):
+    dev = need_gpu()
+    say("ex bf16", B, H, Tq, Tk, off, win, D)
+    inp = shifted_inputs(B, H, Tq, Tk, D, "bf16", seed=Tq + Tk + D)
+    compare(run_ex(inp, dev, off, win), run_oracle(inp, offset=off, window=win), "bf16",
+            label="bf16 Tq=%d Tk=%d off=%d win=%d D=%d" % (Tq, Tk, off, win, D))
+
+
+@pytest.mark.parametrize("D", [16, 32, 64])
+@pytest.mark.parametrize("B,H,Tq,Tk,off,win", SHAPES[1:])
+def test_shifted_and_banded_f32(B, H, Tq, Tk, off, win, D):
+    dev = need_gpu()
+    say("ex f32", B, H, Tq, Tk, off, win, D)
+    inp = shifted_inputs(B, H, Tq, Tk, D, "f32", seed=Tq + Tk + D)
+    compare(run_ex(inp, dev, off, win), run_oracle(inp, offset=off, window=win), "f32",
+            label="f32 Tq=%d Tk=%d off=%d win=%d D=%d" % (Tq, Tk, off, win, D))
+
+
+@pytest.mark.parametrize("name,win", [("gpt2_124m", 256), ("gpt3_2048", 256)])
+def test_banded_full_size(name, win):
+    """Banded attention at the full workload shapes, sampled heads."""
+    dev = need_gpu()
+    w = W.WORKLOADS[name]
+    say("banded full", name, win)
+    inp = W.workload_inputs(name, seed=3)
+    heads = sample_heads(w.B, w.H, 4, seed=3)
+    compare(run_ex(inp, dev, 0, win), run_oracle(inp, heads, window=win), w.dtype, heads,
+            label="%s window %d" % (name, win))
+
+
+def test_plain_case_equals_dense_entry_points():
+    """offset 0, window 0, Tq = Tk through the _ex calls is the dense call."""
+    dev = need_gpu()
+    inp = W.make_inputs(2, 3, 333, 128, "bf16", seed=8)
+    a = run_ex(inp, dev, 0, 0)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o, lse = G.fwd(q, k, v, inp["scale"])
+    g = G.bwd(q, k, v, o, do, lse, inp["scale"])
+    torch.cuda.synchronize()
+    for name, t in zip(("o", "lse", "dq", "dk", "dv"), (o, lse) + tuple(g)):
+        assert np.array_equal(a[name], to64(t)), name
