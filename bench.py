@@ -12,6 +12,12 @@ implementation work and is not counted.
 
 Prints one JSON line.  Per-kernel durations come from HIP events recorded on
 the launch stream around every launch of the timed steps.
+
+The line also carries "variants": the strided entry points timed the same
+way (HIP events around each step) on the same head shape -- q, k, v read in
+place from a packed [B, T, 3C] buffer with gradients written into one packed
+buffer; a locally banded causal mask of 256 positions; and one decoding step
+(one query against a 1024-token context, forward only, reported in GB/s).
 """
 
 import argparse
@@ -112,6 +118,104 @@ def cpu_baseline(inp, budget_s):
     }
 
 
+def visible_pairs(Tq, Tk, off, win):
+    """Number of (query, key) pairs the mask lets through."""
+    n = 0
+    for i in range(Tq):
+        hi = min(Tk - 1, i + off)
+        lo = max(0, i + off - win + 1) if win > 0 else 0
+        n += max(0, hi - lo + 1)
+    return n
+
+
+def time_steps(step, steps, warmup, stream):
+    """Average GPU time (ms) of `step` between HIP events on `stream`."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(steps):
+        step()
+    ev[1].record(stream)
+    ev[1].synchronize()
+    return ev[0].elapsed_time(ev[1]) / steps
+
+
+def variants(G, inp, dev, stream, steps):
+    """Time the strided entry points on the workload's head shape."""
+    import ctypes
+
+    import torch
+
+    lib = G.library()
+    sp = stream.cuda_stream
+    q0, k0, v0, do0 = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    B, H, T, D = q0.shape
+    sc = inp["scale"]
+    out = {}
+
+    def ex_step(pb, q, k, v, o, lse, do, dq, dk, dv, ws, fwd_only=False):
+        P = ctypes.byref
+        tq, tk, tv, to = (G._tensor(t) for t in (q, k, v, o))
+        if fwd_only:
+            def step():
+                rc = lib.gptattn_fwd_ex(P(pb), P(tq), P(tk), P(tv), P(to), lse.data_ptr(), sp)
+                if rc:
+                    raise RuntimeError(G.status_string(rc))
+            return step
+        tdo, tdq, tdk, tdv = (G._tensor(t) for t in (do, dq, dk, dv))
+        nbytes = ws.numel()
+
+        def step():
+            rc = lib.gptattn_fwd_ex(P(pb), P(tq), P(tk), P(tv), P(to), lse.data_ptr(), sp)
+            rc = rc or lib.gptattn_bwd_ex(P(pb), P(tq), P(tk), P(tv), P(to), P(tdo),
+                                          lse.data_ptr(), P(tdq), P(tdk), P(tdv),
+                                          ws.data_ptr(), nbytes, sp)
+            if rc:
+                raise RuntimeError(G.status_string(rc))
+        return step
+
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    ws = torch.empty(B * H * T * 4, dtype=torch.uint8, device=dev)
+
+    # packed [B, T, 3C] projection output and packed gradient buffer
+    x = torch.cat([t.transpose(1, 2).reshape(B, T, H * D) for t in (q0, k0, v0)], dim=-1)
+    q, k, v = G.split_qkv(x.contiguous(), H)
+    y = torch.empty(B, T, H * D, dtype=q0.dtype, device=dev)
+    o = y.view(B, T, H, D).transpose(1, 2)
+    gx = torch.empty(B, T, 3 * H * D, dtype=q0.dtype, device=dev)
+    dq, dk, dv = G.split_qkv(gx, H)
+    pb = G._problem(q, k, sc, 0, 0)
+    ms = time_steps(ex_step(pb, q, k, v, o, lse, do0, dq, dk, dv, ws), steps, 3, stream)
+    fl = 12 * D * visible_pairs(T, T, 0, 0) * B * H
+    out["packed_qkv"] = {"B": B, "H": H, "T": T, "D": D, "ms": round(ms, 5),
+                         "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+
+    # locally banded causal mask, 256 positions
+    o2 = torch.empty_like(q0)
+    dq2, dk2, dv2 = (torch.empty_like(q0) for _ in range(3))
+    win = 256
+    pb = G._problem(q0, k0, sc, 0, win)
+    ms = time_steps(ex_step(pb, q0, k0, v0, o2, lse, do0, dq2, dk2, dv2, ws), steps, 3, stream)
+    fl = 12 * D * visible_pairs(T, T, 0, win) * B * H
+    out["banded_w256"] = {"B": B, "H": H, "T": T, "D": D, "window": win, "ms": round(ms, 5),
+                          "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+
+    # one decoding step: one query against the T-token context (forward only)
+    qd = q0[:, :, T - 1:].contiguous()
+    od = torch.empty_like(qd)
+    lsed = torch.empty((B, H, 1), dtype=torch.float32, device=dev)
+    pb = G._problem(qd, k0, sc, T - 1, 0)
+    ms = time_steps(ex_step(pb, qd, k0, v0, od, lsed, None, None, None, None, None,
+                            fwd_only=True), steps, 3, stream)
+    nbytes = B * H * (2 * T * D * 2 + 2 * D * 2 + 4)
+    out["decode_1x%d" % T] = {"B": B, "H": H, "Tq": 1, "Tk": T, "D": D, "ms": round(ms, 5),
+                              "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,6 +226,8 @@ def main():
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--cold-steps", type=int, default=20,
                     help="extra steps timed with the caches flushed before each one")
+    ap.add_argument("--variant-steps", type=int, default=20,
+                    help="timed steps per strided-entry-point variant (0 = skip them)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (calibrates the "
                          "HBM byte counters against a copy of known size) and exit")
@@ -247,6 +353,11 @@ def main():
         }
     traffic = measured_traffic(dom)
 
+    var = None
+    if args.variant_steps > 0:
+        print("bench: strided entry points", file=sys.stderr, flush=True)
+        var = variants(G, inp, dev, stream, args.variant_steps)
+
     base = None
     if args.cpu_budget > 0:
         print("bench: oracle CPU baseline (%.0f s budget)" % args.cpu_budget,
@@ -281,6 +392,7 @@ def main():
             "traffic": traffic,
         },
         "cpu_baseline": base,
+        "variants": var,
     }
     print(json.dumps(out), flush=True)
 

@@ -418,18 +418,24 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
                                           f32x16* dvt, f32x16* dkt, int q0, Span seers, int g,
                                           int c, int tro, const Problem& pb) {
   constexpr int LD = D + 8, DS = D / 16, DE = D / 32, NH = BM / 32;
+  // All score products of the tile first, so that the matrix cores work on
+  // block h + 1 while the vector units turn block h into P and dS.
+  f32x16 st[NH], dp[NH];
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const f32x16 nd = *reinterpret_cast<const f32x16*>(es + 32 * h + 16 * g);
+    // S = Q K^T and dP - delta = dO V^T - delta: rows = queries, columns = keys
+    st[h] = mfma32x32x16(ld_frag16(qb + (32 * h + c) * LD + 8 * g), kf[0], zero16());
+    dp[h] = mfma32x32x16(ld_frag16(db + (32 * h + c) * LD + 8 * g), vf[0], nd);
+#pragma unroll
+    for (int s = 1; s < DS; ++s) {
+      st[h] = mfma32x32x16(ld_frag16(qb + (32 * h + c) * LD + 16 * s + 8 * g), kf[s], st[h]);
+      dp[h] = mfma32x32x16(ld_frag16(db + (32 * h + c) * LD + 16 * s + 8 * g), vf[s], dp[h]);
+    }
+  }
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const f32x16 nl = *reinterpret_cast<const f32x16*>(ls + 32 * h + 16 * g);
-    const f32x16 nd = *reinterpret_cast<const f32x16*>(es + 32 * h + 16 * g);
-    // S = Q K^T and dP - delta = dO V^T - delta: rows = queries, columns = keys
-    f32x16 st = mfma32x32x16(ld_frag16(qb + (32 * h + c) * LD + 8 * g), kf[0], zero16());
-    f32x16 dp = mfma32x32x16(ld_frag16(db + (32 * h + c) * LD + 8 * g), vf[0], nd);
-#pragma unroll
-    for (int s = 1; s < DS; ++s) {
-      st = mfma32x32x16(ld_frag16(qb + (32 * h + c) * LD + 16 * s + 8 * g), kf[s], st);
-      dp = mfma32x32x16(ld_frag16(db + (32 * h + c) * LD + 16 * s + 8 * g), vf[s], dp);
-    }
     bf16x8 pf[2], sf[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -437,10 +443,10 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = 8 * t + j;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], pb.sl2, nl[r]));
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[h][r], pb.sl2, nl[r]));
         if (MASK && !inside(q0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3), seers)) pv = 0.0f;
         p[j] = pv;
-        dsv[j] = pv * dp[r];
+        dsv[j] = pv * dp[h][r];
       }
       pf[t] = pack_bf16x8(p);
       sf[t] = pack_bf16x8(dsv);
