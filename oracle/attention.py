@@ -19,7 +19,12 @@ lecture description page in its own order:
   1/sqrt(head_size); the scale is an explicit argument here;
 * chapter "multi-headed self-attention", exercise EX1 and the chapter
   "batched multi-headed self-attention": heads are one more batch dimension,
-  and note 3 says batch elements never communicate.
+  and note 3 says batch elements never communicate;
+* chapter "scaling up the model! ... adding dropout" (with the nanoGPT
+  README's `--dropout` flag): optional dropout on the attention weights.
+  Read as: the softmax weights P are multiplied by a keep mask M and by
+  1 / (1 - p) before they weight the values; lse is the normaliser of the
+  softmax itself, before dropout.  M comes from oracle.philox.keep_mask.
 
 Layout: every tensor is ``[B, H, T, D]`` (``lse`` is ``[B, H, T]``).  Inputs
 of any float dtype are upcast exactly to float64; ``scale`` is taken as the
@@ -33,9 +38,14 @@ scalar loss L = sum(O * dO), so dL/dO = dO:
     dS_ij = P_ij * (dP_ij - sum_k P_ik dP_ik)        (softmax Jacobian)
     dQ = scale * dS K
     dK = scale * dS^T Q
+
+With dropout, Pd = P * M / (1 - p) replaces P in O = Pd V and dV = Pd^T dO,
+and dP = (dO V^T) * M / (1 - p) enters the softmax Jacobian.
 """
 
 import numpy as np
+
+from oracle import philox
 
 
 def _as_f64(x):
@@ -101,52 +111,79 @@ def probabilities(q, k, scale, offset=0, window=0):
     return _softmax_rows(scores(q, k, scale, offset, window))[0]
 
 
-def forward_head(q, k, v, scale, offset=0, window=0):
+def _drop_factor(keep, p):
+    """Per-weight dropout factor M / (1 - p) (all ones without dropout)."""
+    if keep is None:
+        return None
+    return keep.astype(np.float64) / (1.0 - float(np.float32(p)))
+
+
+def forward_head(q, k, v, scale, offset=0, window=0, keep=None, p=0.0):
     """One (batch, head): returns ``(O [Tq, D], lse [Tq])`` in float64.
 
     A query row that sees no key (possible only with a negative offset) has
-    O = 0 and lse = -inf.
+    O = 0 and lse = -inf.  ``keep`` ([Tq, Tk] booleans) applies dropout with
+    probability ``p`` to the weights.
     """
-    p, lse = _softmax_rows(scores(q, k, scale, offset, window))
-    o = p @ _as_f64(v)
+    w, lse = _softmax_rows(scores(q, k, scale, offset, window))
+    f = _drop_factor(keep, p)
+    if f is not None:
+        w = w * f
+    o = w @ _as_f64(v)
     return o, lse
 
 
-def backward_head(q, k, v, do, scale, offset=0, window=0):
+def backward_head(q, k, v, do, scale, offset=0, window=0, keep=None, p=0.0):
     """One (batch, head): returns ``(dQ [Tq, D], dK [Tk, D], dV [Tk, D])``."""
     q = _as_f64(q)
     k = _as_f64(k)
     v = _as_f64(v)
     do = _as_f64(do)
     sc = _scale64(scale)
-    p = probabilities(q, k, scale, offset, window)
-    dv = p.T @ do
+    w = probabilities(q, k, scale, offset, window)
+    f = _drop_factor(keep, p)
+    wd = w if f is None else w * f
+    dv = wd.T @ do
     dp = do @ v.T
-    row = (p * dp).sum(axis=1, keepdims=True)
-    ds = p * (dp - row)
+    if f is not None:
+        dp = dp * f
+    row = (w * dp).sum(axis=1, keepdims=True)
+    ds = w * (dp - row)
     dq = sc * (ds @ k)
     dk = sc * (ds.T @ q)
     return dq, dk, dv
 
 
-def forward(q, k, v, scale, heads=None, offset=0, window=0):
+def _keep(b, h, H, Tq, Tk, dropout, seed, stream):
+    if dropout <= 0:
+        return None
+    return philox.keep_mask(b * H + h, Tq, Tk, dropout, seed, stream)
+
+
+def forward(q, k, v, scale, heads=None, offset=0, window=0, dropout=0.0, seed=0, stream=0):
     """Batched forward over ``[B, H, Tq, D]`` queries and ``[B, H, Tk, D]``
     keys/values.
 
     ``heads`` optionally lists the (b, h) pairs to compute; the others are
     left as NaN so that a caller cannot mistake them for results.
+    ``dropout``/``seed``/``stream`` select the keep mask of each head
+    (oracle.philox.keep_mask with n = b * H + h).
     Returns ``(O [B,H,Tq,D], lse [B,H,Tq])`` in float64.
     """
     q = np.asarray(q)
     B, H, Tq, D = q.shape
+    Tk = np.asarray(k).shape[2]
     o = np.full((B, H, Tq, D), np.nan)
     lse = np.full((B, H, Tq), np.nan)
     for b, h in _heads(B, H, heads):
-        o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], scale, offset, window)
+        keep = _keep(b, h, H, Tq, Tk, dropout, seed, stream)
+        o[b, h], lse[b, h] = forward_head(q[b, h], k[b, h], v[b, h], scale, offset, window,
+                                          keep, dropout)
     return o, lse
 
 
-def backward(q, k, v, do, scale, heads=None, offset=0, window=0):
+def backward(q, k, v, do, scale, heads=None, offset=0, window=0, dropout=0.0, seed=0,
+             stream=0):
     """Batched backward; returns ``(dQ, dK, dV)`` in float64 (dQ like q,
     dK and dV like k).  Heads not listed in ``heads`` are NaN.
     """
@@ -158,6 +195,7 @@ def backward(q, k, v, do, scale, heads=None, offset=0, window=0):
     dk = np.full((B, H, Tk, D), np.nan)
     dv = np.full((B, H, Tk, D), np.nan)
     for b, h in _heads(B, H, heads):
+        keep = _keep(b, h, H, Tq, Tk, dropout, seed, stream)
         dq[b, h], dk[b, h], dv[b, h] = backward_head(
-            q[b, h], k[b, h], v[b, h], do[b, h], scale, offset, window)
+            q[b, h], k[b, h], v[b, h], do[b, h], scale, offset, window, keep, dropout)
     return dq, dk, dv

@@ -15,6 +15,8 @@ correction fixes that only past and present positions are visible.
 Inputs are nested lists indexed ``[b][h][t][d]``; so are the outputs
 (``lse`` is ``[b][h][t]``).  The optional ``offset`` and ``window`` select
 which keys a query sees exactly as in :func:`oracle.attention.visible`.
+``keep`` (nested ``[b][h][i][j]`` booleans) and ``drop`` apply dropout to
+the weights: a kept weight is divided by 1 - drop, a dropped one is 0.
 """
 
 import math
@@ -28,7 +30,13 @@ def _keys(i, Tk, offset, window):
     return list(range(lo, hi + 1))
 
 
-def _head_forward(q, k, v, scale, offset=0, window=0):
+def _factor(keep, i, j, drop):
+    if keep is None:
+        return 1.0
+    return (1.0 / (1.0 - drop)) if keep[i][j] else 0.0
+
+
+def _head_forward(q, k, v, scale, offset=0, window=0, keep=None, drop=0.0):
     D = len(q[0])
     o = []
     lse = []
@@ -53,14 +61,14 @@ def _head_forward(q, k, v, scale, offset=0, window=0):
         for d in range(D):
             acc = 0.0
             for n, j in enumerate(keys):
-                acc += w[n] * v[j][d]
+                acc += w[n] * _factor(keep, i, j, drop) * v[j][d]
             row.append(acc / z)
         o.append(row)
         lse.append(m + math.log(z))
     return o, lse
 
 
-def _head_backward(q, k, v, do, scale, offset=0, window=0):
+def _head_backward(q, k, v, do, scale, offset=0, window=0, keep=None, drop=0.0):
     D = len(q[0])
     dq = [[0.0] * D for _ in range(len(q))]
     dk = [[0.0] * D for _ in range(len(k))]
@@ -81,14 +89,16 @@ def _head_backward(q, k, v, do, scale, offset=0, window=0):
         for x in w:
             z += x
         p = [x / z for x in w]
-        # o_i = sum_j p_ij v_j, so dL/dp_ij = do_i . v_j and dL/dv_j += p_ij do_i
+        # o_i = sum_j p_ij f_ij v_j (f: dropout factor, 1 without dropout), so
+        # dL/dp_ij = f_ij (do_i . v_j) and dL/dv_j += p_ij f_ij do_i
         g = []
         for n, j in enumerate(keys):
+            f = _factor(keep, i, j, drop)
             acc = 0.0
             for d in range(D):
                 acc += do[i][d] * v[j][d]
-                dv[j][d] += p[n] * do[i][d]
-            g.append(acc)
+                dv[j][d] += p[n] * f * do[i][d]
+            g.append(f * acc)
         # softmax: dL/ds_ij = p_ij (g_ij - sum_k p_ik g_ik)
         mean = 0.0
         for n in range(len(keys)):
@@ -102,13 +112,18 @@ def _head_backward(q, k, v, do, scale, offset=0, window=0):
     return dq, dk, dv
 
 
-def forward(q, k, v, scale, offset=0, window=0):
+def _kh(keep, b, h):
+    return None if keep is None else keep[b][h]
+
+
+def forward(q, k, v, scale, offset=0, window=0, keep=None, drop=0.0):
     """Returns ``(o, lse)`` as nested lists."""
     o, lse = [], []
     for b in range(len(q)):
         ob, lb = [], []
         for h in range(len(q[b])):
-            oh, lh = _head_forward(q[b][h], k[b][h], v[b][h], scale, offset, window)
+            oh, lh = _head_forward(q[b][h], k[b][h], v[b][h], scale, offset, window,
+                                   _kh(keep, b, h), drop)
             ob.append(oh)
             lb.append(lh)
         o.append(ob)
@@ -116,13 +131,14 @@ def forward(q, k, v, scale, offset=0, window=0):
     return o, lse
 
 
-def backward(q, k, v, do, scale, offset=0, window=0):
+def backward(q, k, v, do, scale, offset=0, window=0, keep=None, drop=0.0):
     """Returns ``(dq, dk, dv)`` as nested lists for L = sum(O * dO)."""
     dq, dk, dv = [], [], []
     for b in range(len(q)):
         qb, kb, vb = [], [], []
         for h in range(len(q[b])):
-            a, c, e = _head_backward(q[b][h], k[b][h], v[b][h], do[b][h], scale, offset, window)
+            a, c, e = _head_backward(q[b][h], k[b][h], v[b][h], do[b][h], scale, offset, window,
+                                     _kh(keep, b, h), drop)
             qb.append(a)
             kb.append(c)
             vb.append(e)
