@@ -16,8 +16,9 @@ the launch stream around every launch of the timed steps.
 The line also carries "variants": the strided entry points timed the same
 way (HIP events around each step) on the same head shape -- q, k, v read in
 place from a packed [B, T, 3C] buffer with gradients written into one packed
-buffer; a locally banded causal mask of 256 positions; and one decoding step
-(one query against a 1024-token context, forward only, reported in GB/s).
+buffer; a locally banded causal mask of 256 positions; attention dropout with
+p = 0.1; and one decoding step (one query against a 1024-token context,
+forward only, reported in GB/s).
 """
 
 import argparse
@@ -202,6 +203,13 @@ def variants(G, inp, dev, stream, steps):
     fl = 12 * D * visible_pairs(T, T, 0, win) * B * H
     out["banded_w256"] = {"B": B, "H": H, "T": T, "D": D, "window": win, "ms": round(ms, 5),
                           "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
+
+    # attention dropout, p = 0.1 (the keep mask is redrawn in every kernel)
+    pb = G._problem(q0, k0, sc, 0, 0, 0.1, 1234, 0)
+    ms = time_steps(ex_step(pb, q0, k0, v0, o2, lse, do0, dq2, dk2, dv2, ws), steps, 3, stream)
+    fl = 12 * D * visible_pairs(T, T, 0, 0) * B * H
+    out["dropout_p0.1"] = {"B": B, "H": H, "T": T, "D": D, "dropout": 0.1, "ms": round(ms, 5),
+                           "tflops": round(fl / (ms * 1e-3) / 1e12, 2)}
 
     # one decoding step: one query against the T-token context (forward only)
     qd = q0[:, :, T - 1:].contiguous()

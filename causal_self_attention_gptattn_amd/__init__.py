@@ -61,7 +61,9 @@ class Problem(ctypes.Structure):
     """``gptattn_problem``."""
     _fields_ = [("B", ctypes.c_int), ("H", ctypes.c_int), ("Tq", ctypes.c_int),
                 ("Tk", ctypes.c_int), ("D", ctypes.c_int), ("causal_offset", ctypes.c_int),
-                ("window", ctypes.c_int), ("scale", ctypes.c_float), ("dtype", ctypes.c_int)]
+                ("window", ctypes.c_int), ("scale", ctypes.c_float), ("dtype", ctypes.c_int),
+                ("dropout", ctypes.c_float), ("rng_stream", ctypes.c_uint),
+                ("seed", ctypes.c_ulonglong)]
 
 
 _tp = ctypes.POINTER(Tensor)
@@ -267,11 +269,12 @@ def _tensor(t):
     return Tensor(t.data_ptr(), st[0], st[1], st[2])
 
 
-def _problem(q, k, scale, causal_offset, window):
+def _problem(q, k, scale, causal_offset, window, dropout=0.0, seed=0, rng_stream=0):
     B, H, Tq, D = q.shape
     dt = DTYPE_F32 if q.dtype == torch.float32 else DTYPE_BF16
     return Problem(B, H, Tq, k.shape[2], D, int(causal_offset), int(window),
-                   _scale(scale, D), dt)
+                   _scale(scale, D), dt, float(dropout), int(rng_stream) & 0xFFFFFFFF,
+                   int(seed) & 0xFFFFFFFFFFFFFFFF)
 
 
 def _validate_ex(q, k, v, *rows_q):
@@ -295,11 +298,15 @@ def ex_workspace_bytes(q, k, scale=None, causal_offset=0, window=0):
     return library().gptattn_bwd_ex_workspace_bytes(ctypes.byref(pb))
 
 
-def fwd_ex(q, k, v, scale=None, causal_offset=0, window=0, out=None, lse=None):
+def fwd_ex(q, k, v, scale=None, causal_offset=0, window=0, out=None, lse=None, dropout=0.0,
+           seed=0, rng_stream=0):
     """Forward pass over strided ``[B, H, T, D]`` views; returns ``(o, lse)``.
 
     ``out`` may be any view of q's shape with a contiguous last dimension
     (for example a ``[B, T, H, D]`` buffer transposed to ``[B, H, T, D]``).
+    ``dropout`` > 0 drops attention weights; the mask is a function of
+    (``seed``, ``rng_stream``, head, query, key), so the backward call must
+    get the same three values.
     """
     _validate_ex(q, k, v)
     B, H, Tq, D = q.shape
@@ -307,7 +314,7 @@ def fwd_ex(q, k, v, scale=None, causal_offset=0, window=0, out=None, lse=None):
     lse = torch.empty((B, H, Tq), dtype=torch.float32, device=q.device) if lse is None else lse
     _validate_ex(q, k, v, out)
     _rows_ok(lse, q)
-    pb = _problem(q, k, scale, causal_offset, window)
+    pb = _problem(q, k, scale, causal_offset, window, dropout, seed, rng_stream)
     ts = [_tensor(t) for t in (q, k, v, out)]
     with torch.cuda.device(q.device):
         rc = library().gptattn_fwd_ex(ctypes.byref(pb), *[ctypes.byref(t) for t in ts],
@@ -317,7 +324,7 @@ def fwd_ex(q, k, v, scale=None, causal_offset=0, window=0, out=None, lse=None):
 
 
 def bwd_ex(q, k, v, o, do, lse, scale=None, causal_offset=0, window=0, dq=None, dk=None,
-           dv=None, workspace=None):
+           dv=None, workspace=None, dropout=0.0, seed=0, rng_stream=0):
     """Backward pass over strided views; returns ``(dq, dk, dv)``.  The
     gradients may be views into one packed buffer (see :func:`split_qkv`)."""
     _validate_ex(q, k, v, o, do)
@@ -327,7 +334,7 @@ def bwd_ex(q, k, v, o, do, lse, scale=None, causal_offset=0, window=0, dq=None, 
     dk = torch.empty_like(k, **fresh) if dk is None else dk
     dv = torch.empty_like(v, **fresh) if dv is None else dv
     _validate_ex(q, dk, dv, dq)
-    pb = _problem(q, k, scale, causal_offset, window)
+    pb = _problem(q, k, scale, causal_offset, window, dropout, seed, rng_stream)
     lib = library()
     need = lib.gptattn_bwd_ex_workspace_bytes(ctypes.byref(pb))
     if workspace is None:
@@ -348,10 +355,13 @@ class GPTAttnFunction(torch.autograd.Function):
     :func:`split_qkv`)."""
 
     @staticmethod
-    def forward(ctx, q, k, v, scale=None, causal_offset=0, window=0):
-        o, lse = fwd_ex(q, k, v, scale, causal_offset, window)
+    def forward(ctx, q, k, v, scale=None, causal_offset=0, window=0, dropout=0.0, seed=0,
+                rng_stream=0):
+        o, lse = fwd_ex(q, k, v, scale, causal_offset, window, dropout=dropout, seed=seed,
+                        rng_stream=rng_stream)
         ctx.save_for_backward(q, k, v, o, lse)
         ctx.args = (scale, causal_offset, window)
+        ctx.drop = dict(dropout=dropout, seed=seed, rng_stream=rng_stream)
         return o
 
     @staticmethod
@@ -359,11 +369,14 @@ class GPTAttnFunction(torch.autograd.Function):
         q, k, v, o, lse = ctx.saved_tensors
         if do.stride(3) != 1:
             do = do.contiguous()
-        dq, dk, dv = bwd_ex(q, k, v, o, do, lse, *ctx.args)
-        return dq, dk, dv, None, None, None
+        dq, dk, dv = bwd_ex(q, k, v, o, do, lse, *ctx.args, **ctx.drop)
+        return dq, dk, dv, None, None, None, None, None, None
 
 
-def attention(q, k, v, scale=None, causal_offset=0, window=0):
+def attention(q, k, v, scale=None, causal_offset=0, window=0, dropout=0.0, seed=0,
+              rng_stream=0):
     """Differentiable causal self-attention over ``[B, H, T, D]`` views
-    (``Tq`` queries, ``Tk`` keys; mask parameters as in :func:`fwd_ex`)."""
-    return GPTAttnFunction.apply(q, k, v, scale, causal_offset, window)
+    (``Tq`` queries, ``Tk`` keys; mask and dropout parameters as in
+    :func:`fwd_ex`)."""
+    return GPTAttnFunction.apply(q, k, v, scale, causal_offset, window, dropout, seed,
+                                 rng_stream)

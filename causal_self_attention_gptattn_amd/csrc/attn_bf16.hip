@@ -73,10 +73,10 @@ __device__ __forceinline__ bool needs_mask(int i0, int i1, int j0, int j1, const
 // as two 32-key halves with one online-softmax step each, which keeps only
 // half a tile of scores live.  A row that has seen no key yet keeps
 // m = -inf; the guards keep -inf from meeting -inf.
-template <int D, bool MASK>
+template <int D, bool MASK, bool DROP>
 __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf,
                                          f32x16* ot, float& m, float& l, int k0, Span seen, int c,
-                                         int g, int tro, const Problem& pb) {
+                                         int g, int tro, int qi, uint32_t n, const Problem& pb) {
   constexpr int LD = D + 8, DS = D / 16, DE = D / 32;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
@@ -113,11 +113,20 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb,
     bf16x8 pf[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      // dropout: keep bits of keys k0 + 32a + 16t + {0..7} + 4g (two groups of four)
+      uint32_t kb0 = 0, kb1 = 0;
+      if (DROP) {
+        const uint32_t jb = (uint32_t)(k0 + 32 * a + 16 * t) / 4 + g;
+        kb0 = keep_bits(jb, (uint32_t)qi, n, pb);
+        kb1 = keep_bits(jb + 2, (uint32_t)qi, n, pb);
+      }
       float p[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[8 * t + j], pb.sl2, nm));
-        l += p[j];
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[8 * t + j], pb.sl2, nm));
+        l += pv;  // the normaliser is the softmax's own, before dropout
+        if (DROP) pv = (((j < 4 ? kb0 : kb1) >> (j & 3)) & 1u) ? pv * pb.inv_keep : 0.0f;
+        p[j] = pv;
       }
       pf[t] = pack_bf16x8(p);
     }
@@ -131,7 +140,7 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb,
   }
 }
 
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
     View Q, View K, View V, View O, float* __restrict__ LSE, Problem pb, int nqb) {
   constexpr int BM = kBM, BN = kBN;
@@ -202,9 +211,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
     if (kt >= wv.t0 && kt <= wv.t1) {
       const int k0 = kt * BN;
       if (needs_mask(q0w, wlast, k0, k0 + BN - 1, pb)) {
-        fwd_tile<D, true>(Ks[buf], Vs[buf], qf, ot, m, l, k0, seen, c, g, tro, pb);
+        fwd_tile<D, true, DROP>(Ks[buf], Vs[buf], qf, ot, m, l, k0, seen, c, g, tro, qi, n, pb);
       } else {
-        fwd_tile<D, false>(Ks[buf], Vs[buf], qf, ot, m, l, k0, seen, c, g, tro, pb);
+        fwd_tile<D, false, DROP>(Ks[buf], Vs[buf], qf, ot, m, l, k0, seen, c, g, tro, qi, n, pb);
       }
     }
     if (more) {
@@ -239,11 +248,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
 // halves.  nd holds -delta of this lane's query in all 16 slots; it seeds
 // the dP^T accumulator so that the product directly yields dP^T - delta.
 // nl is -lse * log2(e), -inf for a row that sees no key (then P = 0).
-template <int D, bool MASK>
+template <int D, bool MASK, bool DROP>
 __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf,
                                         const bf16x8* df, const f32x16& nd, f32x16* acc, int k0,
-                                        Span seen, int c, int g, int tro, float nl,
-                                        const Problem& pb) {
+                                        Span seen, int c, int g, int tro, float nl, int qi,
+                                        uint32_t n, const Problem& pb) {
   constexpr int LD = D + 8, DS = D / 16, DE = D / 32;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
@@ -258,6 +267,12 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
     bf16x8 sf[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      uint32_t kb0 = 0, kb1 = 0;
+      if (DROP) {
+        const uint32_t jb = (uint32_t)(k0 + 32 * a + 16 * t) / 4 + g;
+        kb0 = keep_bits(jb, (uint32_t)qi, n, pb);
+        kb1 = keep_bits(jb + 2, (uint32_t)qi, n, pb);
+      }
       float ds[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -267,7 +282,15 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
           const int key = k0 + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
           if (!inside(key, seen)) p = 0.0f;
         }
-        ds[j] = p * dp[r];
+        if (DROP) {
+          // dp holds dO.V - delta; the dropped-out weight's gradient is
+          // M / (1 - p) * dO.V, so dS = P * (M / (1 - p) * dO.V - delta)
+          const float delta = -nd[0];
+          const bool keep = ((j < 4 ? kb0 : kb1) >> (j & 3)) & 1u;
+          ds[j] = p * (keep ? __builtin_fmaf(dp[r] + delta, pb.inv_keep, -delta) : -delta);
+        } else {
+          ds[j] = p * dp[r];
+        }
       }
       sf[t] = pack_bf16x8(ds);
     }
@@ -281,7 +304,7 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
   }
 }
 
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void attn_bwd_dq(
     View Q, View K, View V, View O, View dO, const float* __restrict__ LSE, View dQ,
     float* __restrict__ Delta, Problem pb, int nqb) {
@@ -370,9 +393,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void attn_bwd_dq(
     if (kt >= wv.t0 && kt <= wv.t1) {
       const int k0 = kt * BN;
       if (needs_mask(q0w, wlast, k0, k0 + BN - 1, pb)) {
-        dq_tile<D, true>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, seen, c, g, tro, nl, pb);
+        dq_tile<D, true, DROP>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, seen, c, g, tro, nl, qi, n,
+                               pb);
       } else {
-        dq_tile<D, false>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, seen, c, g, tro, nl, pb);
+        dq_tile<D, false, DROP>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, seen, c, g, tro, nl, qi, n,
+                                pb);
       }
     }
     if (more) {
@@ -412,19 +437,20 @@ __device__ __forceinline__ int stat_slot(int q) {
 // hold -lse * log2(e) (-inf for rows that see no key or lie past Tq) and
 // -delta of the tile's queries, permuted by stat_slot; -delta seeds the dP
 // accumulator so that the product yields dP - delta directly.
-template <int D, int BM, bool MASK>
+template <int D, int BM, bool MASK, bool DROP>
 __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db, const float* ls,
                                           const float* es, const bf16x8* kf, const bf16x8* vf,
                                           f32x16* dvt, f32x16* dkt, int q0, Span seers, int g,
-                                          int c, int tro, const Problem& pb) {
+                                          int c, int tro, int kj, uint32_t n, const Problem& pb) {
   constexpr int LD = D + 8, DS = D / 16, DE = D / 32, NH = BM / 32;
   // All score products of the tile first, so that the matrix cores work on
   // block h + 1 while the vector units turn block h into P and dS.
   f32x16 st[NH], dp[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
-    const f32x16 nd = *reinterpret_cast<const f32x16*>(es + 32 * h + 16 * g);
     // S = Q K^T and dP - delta = dO V^T - delta: rows = queries, columns = keys
+    // (with dropout dP starts at 0: delta is subtracted after the mask)
+    const f32x16 nd = DROP ? zero16() : *reinterpret_cast<const f32x16*>(es + 32 * h + 16 * g);
     st[h] = mfma32x32x16(ld_frag16(qb + (32 * h + c) * LD + 8 * g), kf[0], zero16());
     dp[h] = mfma32x32x16(ld_frag16(db + (32 * h + c) * LD + 8 * g), vf[0], nd);
 #pragma unroll
@@ -436,6 +462,23 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const f32x16 nl = *reinterpret_cast<const f32x16*>(ls + 32 * h + 16 * g);
+    // Dropout: keep bit of (query 8u + 4g + t of the block, this lane's key)
+    // in bit t of kq[u].  Lane x of each group of four (keys 4 * (kj / 4) + x)
+    // draws the bits of query 8u + 4g + x for all four keys; a transpose
+    // within the group hands each lane its own key's bits.
+    uint32_t kq[4] = {0u, 0u, 0u, 0u};
+    f32x16 nd;
+    if (DROP) {
+      nd = *reinterpret_cast<const f32x16*>(es + 32 * h + 16 * g);
+      const uint32_t x = (uint32_t)(c & 3);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t mine = keep_bits((uint32_t)kj >> 2,
+                                        (uint32_t)(q0 + 32 * h + 8 * u + 4 * g) + x, n, pb);
+        kq[u] = ((quad_lane<0>(mine) >> x) & 1u) | (((quad_lane<1>(mine) >> x) & 1u) << 1) |
+                (((quad_lane<2>(mine) >> x) & 1u) << 2) | (((quad_lane<3>(mine) >> x) & 1u) << 3);
+      }
+    }
     bf16x8 pf[2], sf[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -445,8 +488,14 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
         const int r = 8 * t + j;
         float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[h][r], pb.sl2, nl[r]));
         if (MASK && !inside(q0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3), seers)) pv = 0.0f;
-        p[j] = pv;
-        dsv[j] = pv * dp[h][r];
+        if (DROP) {
+          const bool keep = (kq[r >> 2] >> (r & 3)) & 1u;
+          p[j] = keep ? pv * pb.inv_keep : 0.0f;                        // for dV
+          dsv[j] = pv * ((keep ? dp[h][r] * pb.inv_keep : 0.0f) + nd[r]);  // nd = -delta
+        } else {
+          p[j] = pv;
+          dsv[j] = pv * dp[h][r];
+        }
       }
       pf[t] = pack_bf16x8(p);
       sf[t] = pack_bf16x8(dsv);
@@ -463,7 +512,7 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
   }
 }
 
-template <int D, int BM>
+template <int D, int BM, bool DROP>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
     View Q, View K, View V, View dO, const float* __restrict__ LSE,
     const float* __restrict__ Delta, View dK, View dV, Problem pb) {
@@ -557,11 +606,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
     const int q0 = qt * BM;
     if (q0 + BM - 1 >= wqlo && q0 <= wqhi) {  // some query of the tile sees a key of this wave
       if (needs_mask(q0, q0 + BM - 1, k0w, k0w + 31, pb)) {
-        dkdv_tile<D, BM, true>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0, seers, g,
-                               c, tro, pb);
+        dkdv_tile<D, BM, true, DROP>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0,
+                                     seers, g, c, tro, kj, n, pb);
       } else {
-        dkdv_tile<D, BM, false>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0, seers, g,
-                                c, tro, pb);
+        dkdv_tile<D, BM, false, DROP>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0,
+                                      seers, g, c, tro, kj, n, pb);
       }
     }
     if (more) store_tile(buf ^ 1);
@@ -598,62 +647,71 @@ View view(const TensorArg& t) {
   return View{static_cast<const uint16_t*>(t.data), t.sb, t.sh, t.st};
 }
 
-Problem problem(const ProblemArg& p) {
-  return Problem{p.B * p.H, p.H, p.Tq, p.Tk, p.off, p.win, p.scale * kLog2e, p.scale};
-}
-
 }  // namespace
+
+Problem make_problem(const ProblemArg& p) {
+  Problem pb{p.B * p.H, p.H, p.Tq, p.Tk, p.off, p.win, p.scale * kLog2e, p.scale,
+             (uint32_t)p.seed, (uint32_t)(p.seed >> 32), p.stream, 0u, 1.0f};
+  if (p.dropout > 0.0f) {
+    const double t = ceil((double)p.dropout * 4294967296.0);
+    pb.thr = t >= 4294967295.0 ? 4294967295u : (uint32_t)t;
+    pb.inv_keep = 1.0f / (1.0f - p.dropout);
+  }
+  return pb;
+}
 
 hipError_t launch_fwd_bf16(const TensorArg& q, const TensorArg& k, const TensorArg& v,
                            const TensorArg& o, float* lse, const ProblemArg& p,
                            hipStream_t stream) {
-  const Problem pb = problem(p);
+  const Problem pb = make_problem(p);
   const int nqb = (p.Tq + kBM - 1) / kBM;
   const long long blocks = (long long)pb.N * nqb;
+  const bool drop = p.dropout > 0.0f;
+#define GPTATTN_FWD(D_, DROP_)                                                                  \
+  launch(attn_fwd<D_, DROP_>, blocks, stream, view(q), view(k), view(v), view(o), lse, pb, nqb)
   switch (p.D) {
-    case 64:
-      return launch(attn_fwd<64>, blocks, stream, view(q), view(k), view(v), view(o), lse, pb,
-                    nqb);
-    case 128:
-      return launch(attn_fwd<128>, blocks, stream, view(q), view(k), view(v), view(o), lse, pb,
-                    nqb);
+    case 64: return drop ? GPTATTN_FWD(64, true) : GPTATTN_FWD(64, false);
+    case 128: return drop ? GPTATTN_FWD(128, true) : GPTATTN_FWD(128, false);
     default: return hipErrorInvalidValue;
   }
+#undef GPTATTN_FWD
 }
 
 hipError_t launch_bwd_dq_bf16(const TensorArg& q, const TensorArg& k, const TensorArg& v,
                               const TensorArg& o, const TensorArg& dO, const float* lse,
                               const TensorArg& dq, float* delta, const ProblemArg& p,
                               hipStream_t stream) {
-  const Problem pb = problem(p);
+  const Problem pb = make_problem(p);
   const int nqb = (p.Tq + kBM - 1) / kBM;
   const long long blocks = (long long)pb.N * nqb;
+  const bool drop = p.dropout > 0.0f;
+#define GPTATTN_DQ(D_, DROP_)                                                                   \
+  launch(attn_bwd_dq<D_, DROP_>, blocks, stream, view(q), view(k), view(v), view(o), view(dO),  \
+         lse, view(dq), delta, pb, nqb)
   switch (p.D) {
-    case 64:
-      return launch(attn_bwd_dq<64>, blocks, stream, view(q), view(k), view(v), view(o),
-                    view(dO), lse, view(dq), delta, pb, nqb);
-    case 128:
-      return launch(attn_bwd_dq<128>, blocks, stream, view(q), view(k), view(v), view(o),
-                    view(dO), lse, view(dq), delta, pb, nqb);
+    case 64: return drop ? GPTATTN_DQ(64, true) : GPTATTN_DQ(64, false);
+    case 128: return drop ? GPTATTN_DQ(128, true) : GPTATTN_DQ(128, false);
     default: return hipErrorInvalidValue;
   }
+#undef GPTATTN_DQ
 }
 
 hipError_t launch_bwd_dkdv_bf16(const TensorArg& q, const TensorArg& k, const TensorArg& v,
                                 const TensorArg& dO, const float* lse, const float* delta,
                                 const TensorArg& dk, const TensorArg& dv, const ProblemArg& p,
                                 hipStream_t stream) {
-  const Problem pb = problem(p);
+  const Problem pb = make_problem(p);
   const long long blocks = (long long)pb.N * ((p.Tk + kKBN - 1) / kKBN);
+  const bool drop = p.dropout > 0.0f;
+#define GPTATTN_DKDV(D_, BM_, DROP_)                                                            \
+  launch(attn_bwd_dkdv<D_, BM_, DROP_>, blocks, stream, view(q), view(k), view(v), view(dO),    \
+         lse, delta, view(dk), view(dv), pb)
   switch (p.D) {
-    case 64:
-      return launch(attn_bwd_dkdv<64, 64>, blocks, stream, view(q), view(k), view(v), view(dO),
-                    lse, delta, view(dk), view(dv), pb);
-    case 128:
-      return launch(attn_bwd_dkdv<128, 32>, blocks, stream, view(q), view(k), view(v), view(dO),
-                    lse, delta, view(dk), view(dv), pb);
+    case 64: return drop ? GPTATTN_DKDV(64, 64, true) : GPTATTN_DKDV(64, 64, false);
+    case 128: return drop ? GPTATTN_DKDV(128, 32, true) : GPTATTN_DKDV(128, 32, false);
     default: return hipErrorInvalidValue;
   }
+#undef GPTATTN_DKDV
 }
 
 }  // namespace gptattn

@@ -123,7 +123,17 @@ struct Problem {
   int N, H, Tq, Tk, off, win;
   float sl2;    // scale * log2(e)
   float scale;
+  // attention dropout (used only by the dropout instantiations)
+  uint32_t seed_lo, seed_hi;  // Philox key
+  uint32_t stream;            // fourth counter word
+  uint32_t thr;               // drop iff draw < thr, thr = ceil(p * 2^32)
+  float inv_keep;             // 1 / (1 - p)
 };
+
+// Kernel-side problem description from the host-side one (launch.h); fills
+// the dropout threshold thr = ceil(p * 2^32) and 1 / (1 - p).
+struct ProblemArg;
+Problem make_problem(const ProblemArg& p);
 
 template <typename P>
 __device__ __forceinline__ P head_of(P p, long long sb, long long sh, int n, int H) {
@@ -159,6 +169,51 @@ __device__ __forceinline__ int queries_lo(int j0, const Problem& pb) {
 }
 __device__ __forceinline__ int queries_hi(int j1, const Problem& pb) {
   return pb.win > 0 ? min(pb.Tq - 1, j1 - pb.off + pb.win - 1) : pb.Tq - 1;
+}
+
+// ---------------------------------------------------------------------------
+// Attention dropout.  Philox4x32-10 (Salmon, Moraes, Dror and Shaw,
+// "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011): per round the
+// words 0 and 2 are multiplied by 0xD2511F53 and 0xCD9E8D57 into 64-bit
+// products; the new words are (hi(w2 product) ^ w1 ^ key0, lo(w2 product),
+// hi(w0 product) ^ w3 ^ key1, lo(w0 product)); the key advances by
+// 0x9E3779B9 and 0xBB67AE85 between rounds.
+//
+// For head-problem n, query i and key j the draw is word j % 4 of the
+// generator on counter (j / 4, i, n, stream) with key (seed_lo, seed_hi);
+// the weight is kept iff draw >= thr and then scaled by 1 / (1 - p).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                               uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c0 = n0;
+    c1 = (uint32_t)p1;
+    c2 = n2;
+    c3 = (uint32_t)p0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return u32x4{c0, c1, c2, c3};
+}
+
+// Keep bits of the four keys 4 * jb .. 4 * jb + 3 for query i (bit k = key
+// 4 * jb + k).
+__device__ __forceinline__ uint32_t keep_bits(uint32_t jb, uint32_t i, uint32_t n,
+                                              const Problem& pb) {
+  const u32x4 w = philox4x32_10(jb, i, n, pb.stream, pb.seed_lo, pb.seed_hi);
+  return (w[0] >= pb.thr ? 1u : 0u) | (w[1] >= pb.thr ? 2u : 0u) |
+         (w[2] >= pb.thr ? 4u : 0u) | (w[3] >= pb.thr ? 8u : 0u);
+}
+
+// Value of v in lane SRC of this lane's group of four (DPP quad permute).
+template <int SRC>
+__device__ __forceinline__ uint32_t quad_lane(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, SRC * 0x55, 0xF, 0xF, false);
 }
 
 // ---------------------------------------------------------------------------

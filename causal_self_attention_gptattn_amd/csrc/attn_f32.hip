@@ -49,7 +49,17 @@ __device__ __forceinline__ void key_range(int i, const Problem& pb, int& lo, int
   hi = i < pb.Tq ? keys_hi(i, pb) : -1;
 }
 
-template <int D>
+// Dropout factor of (query i, key j): 0 or 1 / (1 - p); `bits` caches the
+// keep bits of the four keys of j's group, drawn when j starts a group.
+template <bool DROP>
+__device__ __forceinline__ float drop_factor(int i, int j, int j0, uint32_t n, uint32_t& bits,
+                                             const Problem& pb) {
+  if (!DROP) return 1.0f;
+  if (j == j0 || (j & 3) == 0) bits = keep_bits((uint32_t)j >> 2, (uint32_t)i, n, pb);
+  return ((bits >> (j & 3)) & 1u) ? pb.inv_keep : 0.0f;
+}
+
+template <int D, bool DROP>
 __global__ __launch_bounds__(kRows) void attn_fwd_f32(FView Q, FView K, FView V, FView O,
                                                       float* __restrict__ LSE, Problem pb,
                                                       int nt) {
@@ -77,22 +87,25 @@ __global__ __launch_bounds__(kRows) void attn_fwd_f32(FView Q, FView K, FView V,
     stage_rows<D>(Vs, Vh, V.st, k0, pb.Tk, tid);
     __syncthreads();
     const int j0 = max(0, lo - k0), j1 = min(kRows - 1, hi - k0);
+    uint32_t bits = 0;
     for (int j = j0; j <= j1; ++j) {
       float s = 0.0f;
 #pragma unroll
       for (int d = 0; d < D; ++d) s = __builtin_fmaf(q[d], Ks[j * D + d], s);
       s *= pb.scale;
+      // the normaliser l is the softmax's own; dropout scales what reaches O
+      const float f = drop_factor<DROP>(qi, k0 + j, k0 + j0, n, bits, pb);
       if (s > m) {
         const float corr = expf(m - s);  // 0 for the first key (m = -inf)
         l = l * corr + 1.0f;
 #pragma unroll
-        for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(acc[d], corr, Vs[j * D + d]);
+        for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(acc[d], corr, f * Vs[j * D + d]);
         m = s;
       } else {
         const float p = expf(s - m);
         l += p;
 #pragma unroll
-        for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(p, Vs[j * D + d], acc[d]);
+        for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(p * f, Vs[j * D + d], acc[d]);
       }
     }
     __syncthreads();
@@ -108,7 +121,7 @@ __global__ __launch_bounds__(kRows) void attn_fwd_f32(FView Q, FView K, FView V,
 
 // delta_i = sum_d dO_id O_id, then dQ_i = scale sum_j P_ij (dP_ij - delta_i) K_j
 // over the keys j that query i sees.
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(kRows) void attn_bwd_dq_f32(FView Q, FView K, FView V, FView O,
                                                          FView dO, const float* __restrict__ LSE,
                                                          FView dQ, float* __restrict__ Delta,
@@ -145,6 +158,7 @@ __global__ __launch_bounds__(kRows) void attn_bwd_dq_f32(FView Q, FView K, FView
     stage_rows<D>(Vs, Vh, V.st, k0, pb.Tk, tid);
     __syncthreads();
     const int j0 = max(0, lo - k0), j1 = min(kRows - 1, hi - k0);
+    uint32_t bits = 0;
     for (int j = j0; j <= j1; ++j) {
       float s = 0.0f, dp = 0.0f;
 #pragma unroll
@@ -153,7 +167,8 @@ __global__ __launch_bounds__(kRows) void attn_bwd_dq_f32(FView Q, FView K, FView
         dp = __builtin_fmaf(g[d], Vs[j * D + d], dp);
       }
       const float p = expf(s * pb.scale - lse);
-      const float ds = p * (dp - delta);
+      const float f = drop_factor<DROP>(qi, k0 + j, k0 + j0, n, bits, pb);
+      const float ds = p * (f * dp - delta);
 #pragma unroll
       for (int d = 0; d < D; ++d) acc[d] = __builtin_fmaf(ds, Ks[j * D + d], acc[d]);
     }
@@ -168,7 +183,7 @@ __global__ __launch_bounds__(kRows) void attn_bwd_dq_f32(FView Q, FView K, FView
 
 // dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i P_ij (dP_ij - delta_i) Q_i over
 // the queries i that see key j.
-template <int D>
+template <int D, bool DROP>
 __global__ __launch_bounds__(kRows) void attn_bwd_dkdv_f32(FView Q, FView K, FView V, FView dO,
                                                            const float* __restrict__ LSE,
                                                            const float* __restrict__ Delta,
@@ -215,10 +230,12 @@ __global__ __launch_bounds__(kRows) void attn_bwd_dkdv_f32(FView Q, FView K, FVi
         dp = __builtin_fmaf(Gs[i * D + d], v[d], dp);
       }
       const float p = expf(s * pb.scale - Ls[i]);
-      const float ds = p * (dp - Es[i]);
+      uint32_t bits = 0;
+      const float f = drop_factor<DROP>(q0 + i, kj, kj, n, bits, pb);
+      const float ds = p * (f * dp - Es[i]);
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        dv[d] = __builtin_fmaf(p, Gs[i * D + d], dv[d]);
+        dv[d] = __builtin_fmaf(p * f, Gs[i * D + d], dv[d]);
         dk[d] = __builtin_fmaf(ds, Qs[i * D + d], dk[d]);
       }
     }
@@ -246,16 +263,17 @@ FView view(const TensorArg& t) {
   return FView{static_cast<const float*>(t.data), t.sb, t.sh, t.st};
 }
 
-Problem problem(const ProblemArg& p) {
-  return Problem{p.B * p.H, p.H, p.Tq, p.Tk, p.off, p.win, p.scale * kLog2e, p.scale};
-}
-
 template <int D>
 hipError_t fwd_d(const TensorArg& q, const TensorArg& k, const TensorArg& v, const TensorArg& o,
                  float* lse, const ProblemArg& p, hipStream_t stream) {
   const int nt = (p.Tq + kRows - 1) / kRows;
-  return launch(attn_fwd_f32<D>, (long long)p.B * p.H * nt, stream, view(q), view(k), view(v),
-                view(o), lse, problem(p), nt);
+  const long long blocks = (long long)p.B * p.H * nt;
+  const Problem pb = make_problem(p);
+  if (p.dropout > 0.0f)
+    return launch(attn_fwd_f32<D, true>, blocks, stream, view(q), view(k), view(v), view(o), lse,
+                  pb, nt);
+  return launch(attn_fwd_f32<D, false>, blocks, stream, view(q), view(k), view(v), view(o), lse,
+                pb, nt);
 }
 
 template <int D>
@@ -263,8 +281,13 @@ hipError_t bwd_dq_d(const TensorArg& q, const TensorArg& k, const TensorArg& v,
                     const TensorArg& o, const TensorArg& dO, const float* lse,
                     const TensorArg& dq, float* delta, const ProblemArg& p, hipStream_t stream) {
   const int nt = (p.Tq + kRows - 1) / kRows;
-  return launch(attn_bwd_dq_f32<D>, (long long)p.B * p.H * nt, stream, view(q), view(k),
-                view(v), view(o), view(dO), lse, view(dq), delta, problem(p), nt);
+  const long long blocks = (long long)p.B * p.H * nt;
+  const Problem pb = make_problem(p);
+  if (p.dropout > 0.0f)
+    return launch(attn_bwd_dq_f32<D, true>, blocks, stream, view(q), view(k), view(v), view(o),
+                  view(dO), lse, view(dq), delta, pb, nt);
+  return launch(attn_bwd_dq_f32<D, false>, blocks, stream, view(q), view(k), view(v), view(o),
+                view(dO), lse, view(dq), delta, pb, nt);
 }
 
 template <int D>
@@ -273,8 +296,13 @@ hipError_t bwd_dkdv_d(const TensorArg& q, const TensorArg& k, const TensorArg& v
                       const TensorArg& dk, const TensorArg& dv, const ProblemArg& p,
                       hipStream_t stream) {
   const int nt = (p.Tk + kRows - 1) / kRows;
-  return launch(attn_bwd_dkdv_f32<D>, (long long)p.B * p.H * nt, stream, view(q), view(k),
-                view(v), view(dO), lse, delta, view(dk), view(dv), problem(p), nt);
+  const long long blocks = (long long)p.B * p.H * nt;
+  const Problem pb = make_problem(p);
+  if (p.dropout > 0.0f)
+    return launch(attn_bwd_dkdv_f32<D, true>, blocks, stream, view(q), view(k), view(v),
+                  view(dO), lse, delta, view(dk), view(dv), pb, nt);
+  return launch(attn_bwd_dkdv_f32<D, false>, blocks, stream, view(q), view(k), view(v),
+                view(dO), lse, delta, view(dk), view(dv), pb, nt);
 }
 
 }  // namespace

@@ -120,7 +120,7 @@ gptattn::TensorArg dense(const void* p, int H, int T, int D) {
   return gptattn::TensorArg{p, (long long)H * T * D, (long long)T * D, (long long)D};
 }
 gptattn::ProblemArg causal(int B, int H, int T, int D, float scale) {
-  return gptattn::ProblemArg{B, H, T, T, D, 0, 0, scale};
+  return gptattn::ProblemArg{B, H, T, T, D, 0, 0, scale, 0.0f, 0ull, 0u};
 }
 
 // ---------------------------------------------------------------------------
@@ -217,6 +217,7 @@ int check_problem(const gptattn_problem* p, size_t* elem, bool* head_ok) {
   if ((unsigned __int128)p->B * p->H * p->Tq * 4 >= ((unsigned __int128)1 << 62))
     return GPTATTN_ERROR_INVALID_VALUE;
   if (!scale_ok(p->scale)) return GPTATTN_ERROR_INVALID_VALUE;
+  if (!(p->dropout >= 0.0f && p->dropout < 1.0f)) return GPTATTN_ERROR_INVALID_VALUE;  // NaN too
   *elem = p->dtype == GPTATTN_DTYPE_F32 ? 4 : 2;
   *head_ok = p->dtype == GPTATTN_DTYPE_F32 ? f32_head_ok(p->D) : bf16_head_ok(p->D);
   return GPTATTN_SUCCESS;
@@ -257,8 +258,9 @@ gptattn::TensorArg targ(const gptattn_tensor* t, int rows, int D) {
   return gptattn::TensorArg{t->data, t->stride_b, t->stride_h, rows == 1 ? D : t->stride_t};
 }
 gptattn::ProblemArg parg(const gptattn_problem* p) {
-  return gptattn::ProblemArg{p->B, p->H, p->Tq, p->Tk, p->D, p->causal_offset, p->window,
-                             p->scale};
+  return gptattn::ProblemArg{p->B,    p->H,     p->Tq,      p->Tk,   p->D,
+                             p->causal_offset, p->window, p->scale, p->dropout, p->seed,
+                             p->rng_stream};
 }
 
 // ---------------------------------------------------------------------------

@@ -15,9 +15,14 @@ struct TensorArg {
 
 // Query i of Tq sees key j of Tk when j <= i + off and, with win > 0,
 // j > i + off - win.  Plain causal attention: Tq = Tk, off = 0, win = 0.
+// dropout > 0 drops attention weights with that probability; the keep mask
+// is drawn from Philox4x32-10 keyed by `seed` (see attn_common.h).
 struct ProblemArg {
   int B, H, Tq, Tk, D, off, win;
   float scale;
+  float dropout;
+  unsigned long long seed;
+  unsigned int stream;
 };
 
 // bf16 storage, D in {64, 128}.  lse: [B][H][Tq] float32, contiguous.

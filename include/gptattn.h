@@ -189,6 +189,18 @@ size_t gptattn_bwd_workspace_bytes(int B, int H, int T, int D, int is_f32);
  *    key (possible when causal_offset < 0) gets O = 0 and lse = -inf and
  *    contributes no gradient.
  *
+ * 3. Dropout.  With dropout = p > 0 the softmax weights are dropped with
+ *    probability p and the kept ones scaled by 1/(1 - p) before they weight
+ *    the values (lecture chapter "scaling up the model! ... adding dropout";
+ *    nanoGPT README's --dropout flag); lse stays the softmax's own
+ *    normaliser.  The keep mask is not stored: every kernel redraws it from
+ *    Philox4x32-10 (Salmon et al., "Parallel Random Numbers: As Easy as 1,
+ *    2, 3", SC 2011).  For head-problem n = b*H + h, query i and key j the
+ *    draw is word j % 4 of Philox4x32-10 on counter
+ *    (j / 4, i, n, rng_stream) with key (seed & 0xffffffff, seed >> 32);
+ *    the weight is kept iff draw >= ceil(p * 2^32).  The same problem
+ *    (seed, rng_stream, p) must be passed to the forward and backward calls.
+ *
  * lse and the workspace stay dense: [B][H][Tq] float32.
  * ------------------------------------------------------------------------ */
 
@@ -212,6 +224,9 @@ typedef struct gptattn_problem {
   int window;        /* 0 (unbounded) or band width 1 .. 2^29 */
   float scale;       /* finite, > 0; 1/sqrt(D) for standard attention */
   int dtype;         /* enum gptattn_dtype */
+  float dropout;     /* attention dropout probability p, 0 <= p < 1 (0: none) */
+  unsigned int rng_stream;  /* dropout: fourth counter word (e.g. layer index) */
+  unsigned long long seed;  /* dropout: 64-bit generator key */
 } gptattn_problem;
 
 /*
@@ -219,7 +234,8 @@ typedef struct gptattn_problem {
  *   q : Tq rows; k, v : Tk rows; read only.
  *   o : Tq rows, written.
  *   lse : [B][H][Tq] float32, written.
- * Errors as for gptattn_fwd (dtype outside the enum is INVALID_VALUE).
+ * Errors as for gptattn_fwd (dtype outside the enum, or dropout outside
+ * [0, 1), is INVALID_VALUE).
  */
 int gptattn_fwd_ex(const gptattn_problem* p, const gptattn_tensor* q,
                    const gptattn_tensor* k, const gptattn_tensor* v,

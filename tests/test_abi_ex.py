@@ -19,8 +19,9 @@ def lib():
     return G.library()
 
 
-def prob(B=2, H=2, Tq=8, Tk=8, D=64, off=0, win=0, scale=0.125, dtype=G.DTYPE_BF16):
-    return G.Problem(B, H, Tq, Tk, D, off, win, scale, dtype)
+def prob(B=2, H=2, Tq=8, Tk=8, D=64, off=0, win=0, scale=0.125, dtype=G.DTYPE_BF16,
+         dropout=0.0):
+    return G.Problem(B, H, Tq, Tk, D, off, win, scale, dtype, dropout, 0, 0)
 
 
 def dense(base, p, rows):
@@ -71,6 +72,7 @@ def test_dense_layout_is_accepted(lib):
     dict(off=2 ** 29 + 1), dict(off=-2 ** 29 - 1), dict(Tq=2 ** 29 + 1), dict(win=2 ** 29 + 1),
     dict(scale=0.0), dict(scale=float("nan")), dict(dtype=2), dict(dtype=-1),
     dict(B=2 ** 20, H=2 ** 10, Tq=2 ** 12, Tk=2 ** 12),
+    dict(dropout=-0.1), dict(dropout=1.0), dict(dropout=float("nan")), dict(dropout=float("inf")),
 ])
 def test_bad_problem(lib, kw):
     p = prob(**kw)
@@ -189,3 +191,9 @@ def test_single_row_ignores_its_stride(lib):
     for t in (ins[0], ins[3], ins[4], outs[0]):
         t.stride_t = 0
     assert bwd_ex(lib, p, ins, outs) == WORKSPACE
+
+
+def test_dropout_range_is_accepted(lib):
+    for p_ in (0.0, 0.1, 0.999):
+        p = prob(dropout=p_)
+        assert bwd_ex(lib, p, dense_ins(p), dense_outs(p)) == WORKSPACE

@@ -1,0 +1,121 @@
+"""GPU parity of attention dropout against the oracle.
+
+The keep mask is redrawn by each kernel from Philox4x32-10; the oracle draws
+it with its own implementation of the same generator (oracle/philox.py).
+The float32 path is compared at 1e-5, where a single wrong keep bit would
+show (a weight of ~1/T moves the output by ~|v|/T).  The bf16 cases use
+iid N(0, 1) inputs and short rows so that a wrong bit is well above the
+bf16 tolerance too.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import causal_self_attention_gptattn_amd as G
+from causal_self_attention_gptattn_amd import workloads as W
+
+from gpu_helpers import compare, need_gpu, run_oracle, sample_heads, say, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def run_drop(inp, dev, off, win, p, seed, stream):
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    kw = dict(dropout=p, seed=seed, rng_stream=stream)
+    o, lse = G.fwd_ex(q, k, v, inp["scale"], off, win, **kw)
+    dq, dk, dv = G.bwd_ex(q, k, v, o, do, lse, inp["scale"], off, win, **kw)
+    torch.cuda.synchronize()
+    return {"o": to64(o), "lse": to64(lse), "dq": to64(dq), "dk": to64(dk), "dv": to64(dv)}
+
+
+def oracle_drop(inp, off, win, p, seed, stream, heads=None):
+    from oracle import attention as A
+    q, k, v, do = (inp[n].to(torch.float64).numpy() for n in ("q", "k", "v", "do"))
+    kw = dict(heads=heads, offset=off, window=win, dropout=p, seed=seed, stream=stream)
+    o, lse = A.forward(q, k, v, inp["scale"], **kw)
+    dq, dk, dv = A.backward(q, k, v, do, inp["scale"], **kw)
+    return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
+
+
+def shifted(B, H, Tq, Tk, D, dtype, seed):
+    T = max(Tq, Tk)
+    inp = W.make_inputs(B, H, T, D, dtype, seed, "iid")
+    out = dict(inp)
+    for n in ("q", "do"):
+        out[n] = inp[n][:, :, T - Tq:].contiguous()
+    for n in ("k", "v"):
+        out[n] = inp[n][:, :, :Tk].contiguous()
+    return out
+
+
+CASES = [  # (B, H, Tq, Tk, off, win, p)
+    (1, 2, 7, 7, 0, 0, 0.5),
+    (1, 2, 65, 65, 0, 0, 0.1),
+    (2, 3, 130, 130, 0, 0, 0.3),
+    (1, 2, 1, 77, 76, 0, 0.2),
+    (1, 2, 100, 150, 50, 40, 0.25),
+    (1, 2, 90, 90, -10, 0, 0.15),
+]
+
+
+@pytest.mark.parametrize("D", [16, 32, 64])
+@pytest.mark.parametrize("B,H,Tq,Tk,off,win,p", CASES)
+def test_dropout_f32(B, H, Tq, Tk, off, win, p, D):
+    dev = need_gpu()
+    say("dropout f32", B, H, Tq, Tk, off, win, p, D)
+    inp = shifted(B, H, Tq, Tk, D, "f32", seed=Tq + D)
+    seed, stream = 0x1234567890ABCDEF + D, 3
+    compare(run_drop(inp, dev, off, win, p, seed, stream),
+            oracle_drop(inp, off, win, p, seed, stream), "f32",
+            label="dropout f32 Tq=%d Tk=%d p=%.2f D=%d" % (Tq, Tk, p, D))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B,H,Tq,Tk,off,win,p", CASES)
+def test_dropout_bf16(B, H, Tq, Tk, off, win, p, D):
+    dev = need_gpu()
+    say("dropout bf16", B, H, Tq, Tk, off, win, p, D)
+    inp = shifted(B, H, Tq, Tk, D, "bf16", seed=Tq + D + 1)
+    seed, stream = 987654321 + D, 11
+    compare(run_drop(inp, dev, off, win, p, seed, stream),
+            oracle_drop(inp, off, win, p, seed, stream), "bf16",
+            label="dropout bf16 Tq=%d Tk=%d p=%.2f D=%d" % (Tq, Tk, p, D))
+
+
+def test_dropout_full_size_gpt2():
+    """The GPT-2 124M shape with p = 0.1 (nanoGPT's usual fine-tuning rate
+    for GPT-2-sized models), sampled heads."""
+    dev = need_gpu()
+    w = W.WORKLOADS["gpt2_124m"]
+    inp = W.workload_inputs("gpt2_124m", seed=4)
+    heads = sample_heads(w.B, w.H, 4, seed=4)
+    compare(run_drop(inp, dev, 0, 0, 0.1, 42, 0), oracle_drop(inp, 0, 0, 0.1, 42, 0, heads),
+            "bf16", heads, label="gpt2_124m dropout 0.1")
+
+
+def test_dropout_mask_changes_with_seed_and_stream():
+    dev = need_gpu()
+    inp = shifted(1, 2, 64, 64, 64, "bf16", seed=5)
+    a = run_drop(inp, dev, 0, 0, 0.5, 1, 0)["o"]
+    b = run_drop(inp, dev, 0, 0, 0.5, 2, 0)["o"]
+    c = run_drop(inp, dev, 0, 0, 0.5, 1, 1)["o"]
+    a2 = run_drop(inp, dev, 0, 0, 0.5, 1, 0)["o"]
+    assert np.array_equal(a, a2)
+    assert not np.allclose(a, b) and not np.allclose(a, c)
+
+
+def test_dropout_autograd_packed():
+    dev = need_gpu()
+    B, H, T, D = 1, 3, 96, 64
+    inp = W.make_inputs(B, H, T, D, "bf16", seed=8, recipe="iid")
+    x = torch.cat([inp[n].transpose(1, 2).reshape(B, T, H * D) for n in ("q", "k", "v")],
+                  dim=-1).to(dev).contiguous().requires_grad_(True)
+    q, k, v = G.split_qkv(x, H)
+    o = G.attention(q, k, v, inp["scale"], dropout=0.3, seed=99, rng_stream=2)
+    o.backward(inp["do"].to(dev))
+    torch.cuda.synchronize()
+    gq, gk, gv = G.split_qkv(x.grad, H)
+    ref = oracle_drop(inp, 0, 0, 0.3, 99, 2)
+    got = {"o": to64(o), "lse": ref["lse"], "dq": to64(gq), "dk": to64(gk), "dv": to64(gv)}
+    compare(got, ref, "bf16", label="dropout autograd packed")
