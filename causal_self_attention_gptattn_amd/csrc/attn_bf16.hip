@@ -254,16 +254,23 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
                                         Span seen, int c, int g, int tro, float nl, int qi,
                                         uint32_t n, const Problem& pb) {
   constexpr int LD = D + 8, DS = D / 16, DE = D / 32;
+  // Both halves' score products first, so that the matrix cores work on
+  // half 1 while the vector units turn half 0 into dS (at two waves per
+  // SIMD this wins over three waves without the overlap).
+  // S^T = K Q^T and dP^T - delta = V dO^T - delta: rows = keys, columns = queries
+  f32x16 st[2], dp[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
-    // S^T = K Q^T and dP^T - delta = V dO^T - delta: rows = keys, columns = queries
-    f32x16 st = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 8 * g), qf[0], zero16());
-    f32x16 dp = mfma32x32x16(ld_frag16(vb + (32 * a + c) * LD + 8 * g), df[0], nd);
+    st[a] = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 8 * g), qf[0], zero16());
+    dp[a] = mfma32x32x16(ld_frag16(vb + (32 * a + c) * LD + 8 * g), df[0], nd);
 #pragma unroll
     for (int s = 1; s < DS; ++s) {
-      st = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 16 * s + 8 * g), qf[s], st);
-      dp = mfma32x32x16(ld_frag16(vb + (32 * a + c) * LD + 16 * s + 8 * g), df[s], dp);
+      st[a] = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 16 * s + 8 * g), qf[s], st[a]);
+      dp[a] = mfma32x32x16(ld_frag16(vb + (32 * a + c) * LD + 16 * s + 8 * g), df[s], dp[a]);
     }
+  }
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
     bf16x8 sf[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -277,7 +284,7 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int r = 8 * t + j;
-        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[r], pb.sl2, nl));
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[a][r], pb.sl2, nl));
         if (MASK) {
           const int key = k0 + 32 * a + 8 * (r >> 2) + 4 * g + (r & 3);
           if (!inside(key, seen)) p = 0.0f;
@@ -287,9 +294,9 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
           // M / (1 - p) * dO.V, so dS = P * (M / (1 - p) * dO.V - delta)
           const float delta = -nd[0];
           const bool keep = ((j < 4 ? kb0 : kb1) >> (j & 3)) & 1u;
-          ds[j] = p * (keep ? __builtin_fmaf(dp[r] + delta, pb.inv_keep, -delta) : -delta);
+          ds[j] = p * (keep ? __builtin_fmaf(dp[a][r] + delta, pb.inv_keep, -delta) : -delta);
         } else {
-          ds[j] = p * dp[r];
+          ds[j] = p * dp[a][r];
         }
       }
       sf[t] = pack_bf16x8(ds);
@@ -305,7 +312,7 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
 }
 
 template <int D, bool DROP>
-__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 1) void attn_bwd_dq(
+__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dq(
     View Q, View K, View V, View O, View dO, const float* __restrict__ LSE, View dQ,
     float* __restrict__ Delta, Problem pb, int nqb) {
   constexpr int BM = kBM, BN = kBN;
