@@ -670,6 +670,7 @@ Problem make_problem(const ProblemArg& p) {
 hipError_t launch_fwd_bf16(const TensorArg& q, const TensorArg& k, const TensorArg& v,
                            const TensorArg& o, float* lse, const ProblemArg& p,
                            hipStream_t stream) {
+  if (decode_applies(p)) return launch_decode_bf16(q, k, v, o, lse, p, stream);
   const Problem pb = make_problem(p);
   const int nqb = (p.Tq + kBM - 1) / kBM;
   const long long blocks = (long long)pb.N * nqb;

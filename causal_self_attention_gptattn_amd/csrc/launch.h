@@ -40,6 +40,14 @@ hipError_t launch_bwd_dkdv_bf16(const TensorArg& q, const TensorArg& k, const Te
                                 const TensorArg& dk, const TensorArg& dv, const ProblemArg& p,
                                 hipStream_t stream);
 
+// Short query blocks (Tq <= 4, Tk >= 64, no dropout, bf16): one workgroup per
+// head streams the keys (attn_decode.hip).  launch_fwd_bf16 routes such
+// problems here itself.
+bool decode_applies(const ProblemArg& p);
+hipError_t launch_decode_bf16(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                              const TensorArg& o, float* lse, const ProblemArg& p,
+                              hipStream_t stream);
+
 // float32 storage, D in {16, 32, 64}; same arguments.
 hipError_t launch_fwd_f32(const TensorArg& q, const TensorArg& k, const TensorArg& v,
                           const TensorArg& o, float* lse, const ProblemArg& p,

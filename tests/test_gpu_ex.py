@@ -153,6 +153,46 @@ def test_banded_full_size(name, win):
             label="%s window %d" % (name, win))
 
 
+# short query blocks (Tq <= 4, Tk >= 64) take the streaming decode kernel
+DECODE = [
+    (4, 12, 1, 1024, 1023, 0),     # one decoding step, GPT-2 124M heads
+    (1, 3, 2, 300, 298, 0),
+    (1, 3, 3, 257, 254, 64),       # banded
+    (2, 2, 4, 4000, 3996, 0),      # long context
+    (1, 2, 4, 70, -1, 0),          # query 0 sees no key
+    (1, 2, 4, 100, 10, 3),
+    (1, 1, 1, 64, 63, 0),
+    (1, 2, 4, 64, 300, 0),         # offset past the end: every query sees all keys
+]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("B,H,Tq,Tk,off,win", DECODE)
+def test_decode_bf16(B, H, Tq, Tk, off, win, D):
+    dev = need_gpu()
+    say("decode bf16", B, H, Tq, Tk, off, win, D)
+    inp = shifted_inputs(B, H, Tq, Tk, D, "bf16", seed=Tq + Tk + D + 7)
+    compare(run_ex(inp, dev, off, win), run_oracle(inp, offset=off, window=win), "bf16",
+            label="decode Tq=%d Tk=%d off=%d win=%d D=%d" % (Tq, Tk, off, win, D))
+
+
+def test_decode_packed_cache_layout():
+    """One new token against keys/values read in place from a [B, T, 2, H, D]
+    cache buffer; the query and the output are rows of [B, 1, H, D] buffers."""
+    dev = need_gpu()
+    B, H, T, D = 2, 4, 500, 64
+    inp = shifted_inputs(B, H, 1, T, D, "bf16", seed=21)
+    kv = torch.stack([inp[n].transpose(1, 2) for n in ("k", "v")], dim=2).to(dev).contiguous()
+    k, v = kv[:, :, 0].transpose(1, 2), kv[:, :, 1].transpose(1, 2)
+    q = inp["q"].transpose(1, 2).contiguous().to(dev).transpose(1, 2)
+    y = torch.empty(B, 1, H, D, dtype=torch.bfloat16, device=dev)
+    o, lse = G.fwd_ex(q, k, v, inp["scale"], T - 1, 0, out=y.transpose(1, 2))
+    torch.cuda.synchronize()
+    ref = run_oracle(inp, offset=T - 1)
+    got = {"o": to64(o), "lse": to64(lse), "dq": ref["dq"], "dk": ref["dk"], "dv": ref["dv"]}
+    compare(got, ref, "bf16", label="decode from a packed cache")
+
+
 def test_plain_case_equals_dense_entry_points():
     """offset 0, window 0, Tq = Tk through the _ex calls is the dense call."""
     dev = need_gpu()
