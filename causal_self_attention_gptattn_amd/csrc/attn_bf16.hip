@@ -76,10 +76,12 @@ __device__ __forceinline__ bool needs_mask(int i0, int i1, int j0, int j1, const
 template <int D, bool MASK, bool DROP>
 __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf,
                                          f32x16* ot, float& m, float& l, int k0, Span seen, int c,
-                                         int g, int tro, int qi, uint32_t n, const Problem& pb) {
+                                         int g, int tro, int qi, uint32_t n, int h0, int h1,
+                                         const Problem& pb) {
   constexpr int LD = D + 8, DS = D / 16, DE = D / 32;
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
+    if (MASK && (a < h0 || a > h1)) continue;  // no row of the wave sees these 32 keys
     // S^T = K Q^T for 32 keys: rows = keys, columns = this wave's queries
     f32x16 st = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 8 * g), qf[0], zero16());
 #pragma unroll
@@ -181,6 +183,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
   const TileSpan wv = key_tiles(q0w, q0w + 31, pb, BN);
   const int wlast = min(q0w + 31, pb.Tq - 1);
   const Span seen = keys_of(qi, pb);  // keys this lane's query sees
+  // keys some row of this wave sees (32-key halves outside are skipped)
+  const int wklo = keys_lo(q0w, pb), wkhi = keys_hi(wlast, pb);
 
   RowStage<BN, D, kThreads> ks, vs;
   ks.init(tid, LD, K.st);
@@ -211,9 +215,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
     if (kt >= wv.t0 && kt <= wv.t1) {
       const int k0 = kt * BN;
       if (needs_mask(q0w, wlast, k0, k0 + BN - 1, pb)) {
-        fwd_tile<D, true, DROP>(Ks[buf], Vs[buf], qf, ot, m, l, k0, seen, c, g, tro, qi, n, pb);
+        fwd_tile<D, true, DROP>(Ks[buf], Vs[buf], qf, ot, m, l, k0, seen, c, g, tro, qi, n,
+                                k0 + 31 < wklo ? 1 : 0, k0 + 32 > wkhi ? 0 : 1, pb);
       } else {
-        fwd_tile<D, false, DROP>(Ks[buf], Vs[buf], qf, ot, m, l, k0, seen, c, g, tro, qi, n, pb);
+        fwd_tile<D, false, DROP>(Ks[buf], Vs[buf], qf, ot, m, l, k0, seen, c, g, tro, qi, n, 0, 1,
+                                 pb);
       }
     }
     if (more) {
@@ -252,7 +258,7 @@ template <int D, bool MASK, bool DROP>
 __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf,
                                         const bf16x8* df, const f32x16& nd, f32x16* acc, int k0,
                                         Span seen, int c, int g, int tro, float nl, int qi,
-                                        uint32_t n, const Problem& pb) {
+                                        uint32_t n, int h0, int h1, const Problem& pb) {
   constexpr int LD = D + 8, DS = D / 16, DE = D / 32;
   // Both halves' score products first, so that the matrix cores work on
   // half 1 while the vector units turn half 0 into dS (at two waves per
@@ -261,6 +267,7 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
   f32x16 st[2], dp[2];
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
+    if (MASK && (a < h0 || a > h1)) continue;  // no row of the wave sees these 32 keys
     st[a] = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 8 * g), qf[0], zero16());
     dp[a] = mfma32x32x16(ld_frag16(vb + (32 * a + c) * LD + 8 * g), df[0], nd);
 #pragma unroll
@@ -271,6 +278,7 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
   }
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
+    if (MASK && (a < h0 || a > h1)) continue;
     bf16x8 sf[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -371,6 +379,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dq(
   const TileSpan wv = key_tiles(q0w, q0w + 31, pb, BN);
   const int wlast = min(q0w + 31, pb.Tq - 1);
   const Span seen = keys_of(qi, pb);  // keys this lane's query sees
+  // keys some row of this wave sees (32-key halves outside are skipped)
+  const int wklo = keys_lo(q0w, pb), wkhi = keys_hi(wlast, pb);
 
   RowStage<BN, D, kThreads> ks, vs;
   ks.init(tid, LD, K.st);
@@ -401,10 +411,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dq(
       const int k0 = kt * BN;
       if (needs_mask(q0w, wlast, k0, k0 + BN - 1, pb)) {
         dq_tile<D, true, DROP>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, seen, c, g, tro, nl, qi, n,
-                               pb);
+                               k0 + 31 < wklo ? 1 : 0, k0 + 32 > wkhi ? 0 : 1, pb);
       } else {
         dq_tile<D, false, DROP>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, seen, c, g, tro, nl, qi, n,
-                                pb);
+                                0, 1, pb);
       }
     }
     if (more) {
@@ -448,13 +458,15 @@ template <int D, int BM, bool MASK, bool DROP>
 __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db, const float* ls,
                                           const float* es, const bf16x8* kf, const bf16x8* vf,
                                           f32x16* dvt, f32x16* dkt, int q0, Span seers, int g,
-                                          int c, int tro, int kj, uint32_t n, const Problem& pb) {
+                                          int c, int tro, int kj, uint32_t n, int h0, int h1,
+                                          const Problem& pb) {
   constexpr int LD = D + 8, DS = D / 16, DE = D / 32, NH = BM / 32;
   // All score products of the tile first, so that the matrix cores work on
   // block h + 1 while the vector units turn block h into P and dS.
   f32x16 st[NH], dp[NH];
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
+    if (MASK && (h < h0 || h > h1)) continue;  // no query of the block sees these keys
     // S = Q K^T and dP - delta = dO V^T - delta: rows = queries, columns = keys
     // (with dropout dP starts at 0: delta is subtracted after the mask)
     const f32x16 nd = DROP ? zero16() : *reinterpret_cast<const f32x16*>(es + 32 * h + 16 * g);
@@ -468,6 +480,7 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
   }
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
+    if (MASK && (h < h0 || h > h1)) continue;  // no query of the block sees these keys
     const f32x16 nl = *reinterpret_cast<const f32x16*>(ls + 32 * h + 16 * g);
     // Dropout: keep bit of (query 8u + 4g + t of the block, this lane's key)
     // in bit t of kq[u].  Lane x of each group of four (keys 4 * (kj / 4) + x)
@@ -613,11 +626,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
     const int q0 = qt * BM;
     if (q0 + BM - 1 >= wqlo && q0 <= wqhi) {  // some query of the tile sees a key of this wave
       if (needs_mask(q0, q0 + BM - 1, k0w, k0w + 31, pb)) {
+        // 32-query blocks of the tile that no key of this wave is seen by
+        const int h0 = max(0, (wqlo - q0) >> 5), h1 = min(BM / 32 - 1, (wqhi - q0) >> 5);
         dkdv_tile<D, BM, true, DROP>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0,
-                                     seers, g, c, tro, kj, n, pb);
+                                     seers, g, c, tro, kj, n, h0, h1, pb);
       } else {
         dkdv_tile<D, BM, false, DROP>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0,
-                                      seers, g, c, tro, kj, n, pb);
+                                      seers, g, c, tro, kj, n, 0, BM / 32 - 1, pb);
       }
     }
     if (more) store_tile(buf ^ 1);
