@@ -1,0 +1,116 @@
+"""Seeded sweep of the strided entry points against the float64 oracle.
+
+Forty configurations drawn from a fixed seed cover combinations the
+hand-picked cases do not: both precisions and every compiled head size;
+Tq and Tk from 1 to 600 (including Tq > Tk); causal offsets that leave rows
+without keys or let every row see everything; banded windows; dense,
+[B, T, H, D]-transposed and packed [B, T, 3C] layouts; and dropout.  A long
+sequence (16384 positions) is checked on sampled row blocks of the forward
+pass, which the oracle computes exactly by shifting the causal offset.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import causal_self_attention_gptattn_amd as G
+from causal_self_attention_gptattn_amd import workloads as W
+
+from gpu_helpers import compare, need_gpu, say, to64
+
+pytestmark = pytest.mark.gpu
+
+
+def draw_configs(n, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for idx in range(n):
+        f32 = rng.random() < 0.3
+        D = int(rng.choice([16, 32, 64])) if f32 else int(rng.choice([64, 128]))
+        Tk = int(rng.integers(1, 601))
+        Tq = int(rng.integers(1, 601)) if rng.random() < 0.5 else Tk
+        r = rng.random()
+        if r < 0.4:
+            off = Tk - Tq                      # queries aligned to the end of the keys
+        elif r < 0.6:
+            off = 0
+        else:
+            off = int(rng.integers(-50, Tk + 20))
+        win = 0 if rng.random() < 0.6 else int(rng.integers(1, 300))
+        layout = str(rng.choice(["dense", "bthd", "packed"]))
+        if layout == "packed" and Tq != Tk:
+            layout = "bthd"
+        drop = 0.0 if rng.random() < 0.7 else float(rng.choice([0.1, 0.4]))
+        B, H = int(rng.integers(1, 3)), int(rng.integers(1, 4))
+        out.append((idx, "f32" if f32 else "bf16", B, H, Tq, Tk, D, off, win, layout, drop))
+    return out
+
+
+def place(inp, layout, dev, dtype):
+    """The inputs as views of the requested layout (values unchanged)."""
+    q, k, v, do = (inp[n] for n in ("q", "k", "v", "do"))
+    if layout == "dense":
+        return tuple(t.to(dev) for t in (q, k, v, do)), lambda like: torch.empty_like(like)
+    if layout == "bthd":
+        views = tuple(t.transpose(1, 2).contiguous().to(dev).transpose(1, 2) for t in (q, k, v, do))
+
+        def alloc(like):
+            B, H, T, D = like.shape
+            return torch.empty(B, T, H, D, dtype=like.dtype, device=dev).transpose(1, 2)
+        return views, alloc
+    B, H, T, D = q.shape
+    x = torch.cat([t.transpose(1, 2).reshape(B, T, H * D) for t in (q, k, v)], dim=-1)
+    qv, kv, vv = G.split_qkv(x.to(dev).contiguous(), H)
+    return (qv, kv, vv, do.to(dev)), lambda like: torch.empty_like(like, memory_format=torch.contiguous_format)
+
+
+@pytest.mark.parametrize("cfg", draw_configs(40), ids=lambda c: "c%02d" % c[0])
+def test_sweep(cfg):
+    from oracle import attention as A
+    dev = need_gpu()
+    idx, dtype, B, H, Tq, Tk, D, off, win, layout, drop = cfg
+    say("sweep", cfg)
+    T = max(Tq, Tk)
+    full = W.make_inputs(B, H, T, D, dtype, seed=100 + idx, recipe="iid")
+    inp = dict(full)
+    for n_ in ("q", "do"):
+        inp[n_] = full[n_][:, :, T - Tq:].contiguous()
+    for n_ in ("k", "v"):
+        inp[n_] = full[n_][:, :, :Tk].contiguous()
+    (q, k, v, do), alloc = place(inp, layout, dev, dtype)
+    kw = dict(dropout=drop, seed=77 + idx, rng_stream=idx)
+    o, lse = G.fwd_ex(q, k, v, inp["scale"], off, win, out=alloc(q), **kw)
+    dq, dk, dv = G.bwd_ex(q, k, v, o, do, lse, inp["scale"], off, win, dq=alloc(q), dk=alloc(k),
+                          dv=alloc(v), **kw)
+    torch.cuda.synchronize()
+    got = {"o": to64(o), "lse": to64(lse), "dq": to64(dq), "dk": to64(dk), "dv": to64(dv)}
+    qq, kk, vv, dd = (inp[n_].to(torch.float64).numpy() for n_ in ("q", "k", "v", "do"))
+    okw = dict(offset=off, window=win, dropout=drop, seed=77 + idx, stream=idx)
+    ro, rl = A.forward(qq, kk, vv, inp["scale"], **okw)
+    rdq, rdk, rdv = A.backward(qq, kk, vv, dd, inp["scale"], **okw)
+    ref = {"o": ro, "lse": rl, "dq": rdq, "dk": rdk, "dv": rdv}
+    compare(got, ref, dtype, label="sweep %s" % (cfg,))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_long_sequence_forward_rows(D):
+    """16384 positions, one head: sampled 64-row blocks of O and lse, each
+    computed by the oracle as Tq = 64 queries at offset i0."""
+    from oracle import attention as A
+    dev = need_gpu()
+    T = 16384
+    inp = W.make_inputs(1, 1, T, D, "bf16", seed=D, recipe="iid")
+    q, k, v = (inp[n].to(dev) for n in ("q", "k", "v"))
+    o, lse = G.fwd(q, k, v, inp["scale"])
+    torch.cuda.synchronize()
+    o64, l64 = to64(o), to64(lse)
+    qq, kk, vv = (inp[n].to(torch.float64).numpy() for n in ("q", "k", "v"))
+    for i0 in (0, 4096 - 32, 9000, T - 64):
+        ro, rl = A.forward(qq[:, :, i0:i0 + 64], kk[:, :, :i0 + 64], vv[:, :, :i0 + 64],
+                           inp["scale"], offset=i0)
+        got = {"o": o64[:, :, i0:i0 + 64], "lse": l64[:, :, i0:i0 + 64]}
+        err_o = np.abs(got["o"] - ro).max()
+        lim = 2e-2 + 2.0 ** -8 * np.abs(ro)
+        assert (np.abs(got["o"] - ro) <= lim).all(), "rows %d: O err %.3e" % (i0, err_o)
+        assert np.abs(got["lse"] - rl).max() <= 1e-3, "rows %d: lse" % i0
+        say("long T=%d D=%d rows %d: O err %.2e" % (T, D, i0, err_o))
