@@ -36,6 +36,10 @@ if ROOT not in sys.path:
 METRIC = "causal attn fwd+bwd TFLOP/s at GPT-2 124M shape; % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 flop/clk
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+# Transcendental roof: v_exp_f32 issues at half the fp32 rate (measured: one
+# wave64 instruction per 8 cycles per SIMD), i.e. 256 CU x 4 SIMD x 64 lanes
+# / 8 cycles x 2.4 GHz exponentials per second.
+PEAK_EXP_PER_S = 256 * 4 * 64 / 8 * 2.4e9
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gpt2_124m.json")
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_common.h"]
 
@@ -46,17 +50,19 @@ def unit_flops(N, T, D):
 
 
 def kernel_table(N, T, D):
-    """Algorithmic flops and bytes per launch of each kernel (bf16)."""
+    """Algorithmic flops, bytes and exponentials per launch of each kernel
+    (bf16).  Each kernel takes one exponential per visible score element."""
     u = unit_flops(N, T, D)
     t = N * T * D * 2      # one bf16 [B,H,T,D] tensor
     r = N * T * 4          # one float32 [B,H,T] vector
+    x = N * T * (T + 1) // 2
     return {
         # QK^T and PV; reads Q, K, V, writes O and lse
-        "attn_fwd": {"flops": 2 * u, "bytes": 4 * t + r},
+        "attn_fwd": {"flops": 2 * u, "bytes": 4 * t + r, "exps": x},
         # the dQ product; reads Q, K, V, O, dO, lse, writes dQ and the row term
-        "attn_bwd_dq": {"flops": 1 * u, "bytes": 6 * t + 2 * r},
+        "attn_bwd_dq": {"flops": 1 * u, "bytes": 6 * t + 2 * r, "exps": x},
         # dP, dV and dK products; reads Q, K, V, dO, lse, row term, writes dK, dV
-        "attn_bwd_dkdv": {"flops": 3 * u, "bytes": 6 * t + 2 * r},
+        "attn_bwd_dkdv": {"flops": 3 * u, "bytes": 6 * t + 2 * r, "exps": x},
     }
 
 
@@ -258,6 +264,7 @@ def main():
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
 
     import causal_self_attention_gptattn_amd as G
@@ -325,10 +332,13 @@ def main():
     wall = time.perf_counter() - t0
 
     per_kernel_ms = {name: 0.0 for name, _ in launches}
+    step_ms = []
     for e in evs:
         for i, (name, _) in enumerate(launches):
             per_kernel_ms[name] += e[i].elapsed_time(e[i + 1])
+        step_ms.append(e[0].elapsed_time(e[len(launches)]))
     per_kernel_ms = {k_: t / args.steps for k_, t in per_kernel_ms.items()}
+    q1, med, q3 = (float(x) for x in np.percentile(step_ms, [25, 50, 75]))
 
     # Cold-cache steps: overwrite a 1 GiB buffer before each (outside events).
     cold_ms = None
@@ -354,10 +364,17 @@ def main():
     achieved = table[dom]["flops"] / dom_s / 1e12
     kernels = {}
     for name, t_ms in per_kernel_ms.items():
+        tf = table[name]["flops"] / (t_ms * 1e-3) / 1e12
+        gbs = table[name]["bytes"] / (t_ms * 1e-3) / 1e9
+        eps = table[name]["exps"] / (t_ms * 1e-3)
         kernels[name] = {
             "ms": round(t_ms, 5),
-            "alg_tflops": round(table[name]["flops"] / (t_ms * 1e-3) / 1e12, 2),
-            "alg_gbs": round(table[name]["bytes"] / (t_ms * 1e-3) / 1e9, 1),
+            "alg_tflops": round(tf, 2),
+            "alg_gbs": round(gbs, 1),
+            # fraction of each roof: bf16 MFMA, HBM, transcendental (exp)
+            "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "exp_frac": round(eps / PEAK_EXP_PER_S, 4),
         }
     traffic = measured_traffic(dom)
 
@@ -388,6 +405,11 @@ def main():
         "config": {"workload": w.name, "B": B, "H": H, "T": T, "D": D, "causal": True,
                    "scale": sc, "alg_gflop_per_step": round(flops / 1e9, 3)},
         "pct_of_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        # the FlashAttention-paper convention (7 D T^2 per head-problem, counts
+        # the backward's recomputation); labelled, never mixed with `value`
+        "fa_convention_tflops": round(7 * N * D * T * T / (wall / args.steps) / 1e12, 2),
+        "step_ms_events": {"median": round(med, 5), "min": round(float(min(step_ms)), 5),
+                           "iqr": round(q3 - q1, 5)},
         "kernels": kernels,
         "cold_cache_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
         "roofline": {

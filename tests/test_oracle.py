@@ -311,3 +311,21 @@ def test_selected_heads_only():
     np.testing.assert_array_equal(o_sel[1, 2], o_all[1, 2])
     np.testing.assert_array_equal(lse_sel[0, 0], lse_all[0, 0])
     assert np.isnan(o_sel[0, 1]).all()
+
+
+def test_rounding_variant_is_close_to_the_definition():
+    """The bf16-rounding diagnostic differs from the float64 definition by a
+    few bf16 units, and not at all when every quantity is representable."""
+    from oracle import rounding as R
+    rng = np.random.default_rng(3)
+    q, k, v, do = (rng.standard_normal((12, 8)) * s for s in (0.5, 0.5, 1.0, 0.01))
+    o, _ = A.forward_head(q, k, v, 0.375)
+    ob = R.forward_head(q, k, v, 0.375)
+    assert 0 < np.abs(ob - o).max() < 4 * 2.0 ** -8 * np.abs(o).max()
+    g = A.backward_head(q, k, v, do, 0.375)
+    gb = R.backward_head(q, k, v, do, 0.375)
+    for x, y in zip(g, gb):
+        assert np.linalg.norm(x - y) <= 2e-2 * np.linalg.norm(x)
+    # one key per row (T = 1): P = 1 is exact, so O = bf16(V)
+    v1 = R.bf16(v[:1])
+    np.testing.assert_array_equal(R.forward_head(q[:1], k[:1], v1, 0.375), v1)
