@@ -230,20 +230,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
   }
 
   const float lt = half_sum(l);
-  if (qi < pb.Tq) {
-    const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;  // a row that sees no key outputs 0
-    uint16_t* orow = const_cast<uint16_t*>(head_of(O, n, pb.H)) + (long long)qi * O.st;
-#pragma unroll
-    for (int e = 0; e < DE; ++e)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        u32x2 pk = {pack_bf16x2(ot[e][4 * u] * inv, ot[e][4 * u + 1] * inv),
-                    pack_bf16x2(ot[e][4 * u + 2] * inv, ot[e][4 * u + 3] * inv)};
-        *reinterpret_cast<u32x2*>(orow + 32 * e + 8 * u + 4 * g) = pk;
-      }
-    if (g == 0)
-      LSE[(long long)n * pb.Tq + qi] = lt > 0.0f ? (m + log2f(lt)) * kLn2 : -INFINITY;
-  }
+  const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;  // a row that sees no key outputs 0
+  if (qi < pb.Tq && g == 0)
+    LSE[(long long)n * pb.Tq + qi] = lt > 0.0f ? (m + log2f(lt)) * kLn2 : -INFINITY;
+  // the K tiles are free after the loop's last barrier: 16 rows per wave
+  store_rows<D>(&Ks[0][0] + w * 16 * LD, ot, inv,
+                const_cast<uint16_t*>(head_of(O, n, pb.H)) + (long long)q0w * O.st, O.st,
+                pb.Tq - q0w, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -424,18 +417,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dq(
     __syncthreads();
   }
 
-  if (qi < pb.Tq) {
-    uint16_t* out = const_cast<uint16_t*>(head_of(dQ, n, pb.H)) + (long long)qi * dQ.st;
-    const float sc = pb.scale;
-#pragma unroll
-    for (int e = 0; e < DE; ++e)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        u32x2 pk = {pack_bf16x2(acc[e][4 * u] * sc, acc[e][4 * u + 1] * sc),
-                    pack_bf16x2(acc[e][4 * u + 2] * sc, acc[e][4 * u + 3] * sc)};
-        *reinterpret_cast<u32x2*>(out + 32 * e + 8 * u + 4 * g) = pk;
-      }
-  }
+  store_rows<D>(&Ks[0][0] + w * 16 * LD, acc, pb.scale,
+                const_cast<uint16_t*>(head_of(dQ, n, pb.H)) + (long long)q0w * dQ.st, dQ.st,
+                pb.Tq - q0w, lane);
 }
 
 // ---------------------------------------------------------------------------
@@ -639,23 +623,13 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
     __syncthreads();
   }
 
-  if (kj < pb.Tk) {
-    uint16_t* krow = const_cast<uint16_t*>(head_of(dK, n, pb.H)) + (long long)kj * dK.st;
-    uint16_t* vrow = const_cast<uint16_t*>(head_of(dV, n, pb.H)) + (long long)kj * dV.st;
-    const float sc = pb.scale;
-#pragma unroll
-    for (int e = 0; e < DE; ++e)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int d = 32 * e + 8 * u + 4 * g;
-        u32x2 pk = {pack_bf16x2(dkt[e][4 * u] * sc, dkt[e][4 * u + 1] * sc),
-                    pack_bf16x2(dkt[e][4 * u + 2] * sc, dkt[e][4 * u + 3] * sc)};
-        *reinterpret_cast<u32x2*>(krow + d) = pk;
-        u32x2 pv = {pack_bf16x2(dvt[e][4 * u], dvt[e][4 * u + 1]),
-                    pack_bf16x2(dvt[e][4 * u + 2], dvt[e][4 * u + 3])};
-        *reinterpret_cast<u32x2*>(vrow + d) = pv;
-      }
-  }
+  // the Q / dO tiles are free after the loop's last barrier: 16 rows per wave
+  store_rows<D>(&Qs[0][0] + w * 16 * LD, dkt, pb.scale,
+                const_cast<uint16_t*>(head_of(dK, n, pb.H)) + (long long)k0w * dK.st, dK.st,
+                pb.Tk - k0w, lane);
+  store_rows<D>(&Qs[0][0] + w * 16 * LD, dvt, 1.0f,
+                const_cast<uint16_t*>(head_of(dV, n, pb.H)) + (long long)k0w * dV.st, dV.st,
+                pb.Tk - k0w, lane);
 }
 
 template <typename... Args>

@@ -283,4 +283,43 @@ struct RowStage {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Epilogue: a wave's 32 x D block of results, held in the MFMA result layout
+// (lane (c, g) holds, for row c, columns 32e + 8u + 4g + i in acc[e][4u + i]),
+// goes to HBM as bf16 through a wave-private LDS region of 16 rows at a time,
+// so that every store instruction writes whole rows (D = 64: eight lanes per
+// 128-byte row) instead of 8-byte pieces of 32 rows.  All threads of the
+// workgroup must call it (it contains workgroup barriers); rows at or past
+// `rows_valid` are not written.  lds: this wave's region, 16 * (D + 8)
+// elements, not in use by any other wave.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void store_rows(uint16_t* lds, const f32x16* acc, float mul,
+                                           uint16_t* out, long long st, int rows_valid, int lane) {
+  constexpr int RS = D + 8, DE = D / 32, CPR = D / 8, PASS = 16 * CPR / 64;
+  const int c = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if ((c >> 4) == half) {
+#pragma unroll
+      for (int e = 0; e < DE; ++e)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const u32x2 pk = {pack_bf16x2(acc[e][4 * u] * mul, acc[e][4 * u + 1] * mul),
+                            pack_bf16x2(acc[e][4 * u + 2] * mul, acc[e][4 * u + 3] * mul)};
+          *reinterpret_cast<u32x2*>(lds + (c & 15) * RS + 32 * e + 8 * u + 4 * g) = pk;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int p = 0; p < PASS; ++p) {
+      const int ch = lane + 64 * p, r = ch / CPR, cc = ch % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * RS + 8 * cc);
+      const int row = 16 * half + r;
+      if (row < rows_valid) *reinterpret_cast<u32x4*>(out + (long long)row * st + 8 * cc) = v;
+    }
+    __syncthreads();
+  }
+}
+
 }  // namespace gptattn
