@@ -114,3 +114,26 @@ def test_long_sequence_forward_rows(D):
         assert (np.abs(got["o"] - ro) <= lim).all(), "rows %d: O err %.3e" % (i0, err_o)
         assert np.abs(got["lse"] - rl).max() <= 1e-3, "rows %d: lse" % i0
         say("long T=%d D=%d rows %d: O err %.2e" % (T, D, i0, err_o))
+
+
+def test_many_heads_large_grid():
+    """32768 head-problems of 65 positions: a grid of 32768 workgroups per
+    launch, every head computed; sampled heads checked against the oracle."""
+    from oracle import attention as A
+    dev = need_gpu()
+    B, H, T, D = 256, 128, 65, 64
+    g = torch.Generator().manual_seed(5)
+    q, k, v, do = (torch.randn(B, H, T, D, generator=g).to(torch.bfloat16) for _ in range(4))
+    do = (do.float() * 0.01).to(torch.bfloat16)
+    qd, kd, vd, dd = (t.to(dev) for t in (q, k, v, do))
+    o, lse = G.fwd(qd, kd, vd, 0.125)
+    dq, dk, dv = G.bwd(qd, kd, vd, o, dd, lse, 0.125)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (37, 101), (255, 127), (128, 64)):
+        ro, rl = A.forward(*(t[b:b + 1, h:h + 1].double().numpy() for t in (q, k, v)), 0.125)
+        rq, rk, rv = A.backward(*(t[b:b + 1, h:h + 1].double().numpy() for t in (q, k, v, do)),
+                                0.125)
+        got = {n_: to64(t[b:b + 1, h:h + 1]) for n_, t in
+               (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv))}
+        compare(got, {"o": ro, "lse": rl, "dq": rq, "dk": rk, "dv": rv}, "bf16",
+                label="many heads (%d,%d)" % (b, h))
