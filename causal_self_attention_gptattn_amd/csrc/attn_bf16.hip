@@ -434,6 +434,38 @@ __device__ __forceinline__ int stat_slot(int q) {
   return 32 * (q >> 5) + 16 * ((q & 7) >> 2) + 4 * ((q & 31) >> 3) + (q & 3);
 }
 
+// 16 consecutive row statistics from LDS as four 16-byte reads.  A single
+// 64-byte read would be split by the compiler into pieces that no longer
+// carry the information that they do not overlap the Q / dO copies still in
+// flight, and each piece would then wait for those copies.
+__device__ __forceinline__ f32x16 ld_stats16(const float* p) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  const f32x4 c = *reinterpret_cast<const f32x4*>(p + 8);
+  const f32x4 d = *reinterpret_cast<const f32x4*>(p + 12);
+  return f32x16{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3],
+                c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
+}
+
+// This lane's element offsets into a swizzled Q / dO tile for the reads of
+// dkdv_tile, relative to the first row of a 32-query block.  The swizzle key
+// repeats every 16 rows, so the offsets are the same for every block and the
+// block's position becomes an immediate offset of the read instruction.
+template <int D>
+struct SwzLane {
+  int fo[D / 16];          // row c, chunk 2s + g: fragments of Q and dO
+  int tlo[D / 32], thi[D / 32];  // rows trr and trr + 8, columns 32e + trc: transposed
+  __device__ __forceinline__ void init(int c, int g, int trr, int trc) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) fo[s] = swz<D>(c, 16 * s + 8 * g);
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e) {
+      tlo[e] = swz<D>(trr, 32 * e + trc);
+      thi[e] = swz<D>(trr + 8, 32 * e + trc);
+    }
+  }
+};
+
 // One BM-query tile for one wave (32 keys, one per lane column c).  ls/es
 // hold -lse * log2(e) (-inf for rows that see no key or lie past Tq) and
 // -delta of the tile's queries, permuted by stat_slot; -delta seeds the dP
@@ -442,9 +474,10 @@ template <int D, int BM, bool MASK, bool DROP>
 __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db, const float* ls,
                                           const float* es, const bf16x8* kf, const bf16x8* vf,
                                           f32x16* dvt, f32x16* dkt, int q0, Span seers, int g,
-                                          int c, int tro, int kj, uint32_t n, int h0, int h1,
-                                          const Problem& pb) {
-  constexpr int LD = D + 8, DS = D / 16, DE = D / 32, NH = BM / 32;
+                                          int c, const SwzLane<D>& sw, int kj, uint32_t n, int h0,
+                                          int h1, const Problem& pb) {
+  // Q and dO tiles: unpadded rows of D, 16-byte chunks swizzled (swz)
+  constexpr int DS = D / 16, DE = D / 32, NH = BM / 32;
   // All score products of the tile first, so that the matrix cores work on
   // block h + 1 while the vector units turn block h into P and dS.
   f32x16 st[NH], dp[NH];
@@ -453,19 +486,19 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
     if (MASK && (h < h0 || h > h1)) continue;  // no query of the block sees these keys
     // S = Q K^T and dP - delta = dO V^T - delta: rows = queries, columns = keys
     // (with dropout dP starts at 0: delta is subtracted after the mask)
-    const f32x16 nd = DROP ? zero16() : *reinterpret_cast<const f32x16*>(es + 32 * h + 16 * g);
-    st[h] = mfma32x32x16(ld_frag16(qb + (32 * h + c) * LD + 8 * g), kf[0], zero16());
-    dp[h] = mfma32x32x16(ld_frag16(db + (32 * h + c) * LD + 8 * g), vf[0], nd);
+    const f32x16 nd = DROP ? zero16() : ld_stats16(es + 32 * h + 16 * g);
+    st[h] = mfma32x32x16(ld_frag16(qb + 32 * h * D + sw.fo[0]), kf[0], zero16());
+    dp[h] = mfma32x32x16(ld_frag16(db + 32 * h * D + sw.fo[0]), vf[0], nd);
 #pragma unroll
     for (int s = 1; s < DS; ++s) {
-      st[h] = mfma32x32x16(ld_frag16(qb + (32 * h + c) * LD + 16 * s + 8 * g), kf[s], st[h]);
-      dp[h] = mfma32x32x16(ld_frag16(db + (32 * h + c) * LD + 16 * s + 8 * g), vf[s], dp[h]);
+      st[h] = mfma32x32x16(ld_frag16(qb + 32 * h * D + sw.fo[s]), kf[s], st[h]);
+      dp[h] = mfma32x32x16(ld_frag16(db + 32 * h * D + sw.fo[s]), vf[s], dp[h]);
     }
   }
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     if (MASK && (h < h0 || h > h1)) continue;  // no query of the block sees these keys
-    const f32x16 nl = *reinterpret_cast<const f32x16*>(ls + 32 * h + 16 * g);
+    const f32x16 nl = ld_stats16(ls + 32 * h + 16 * g);
     // Dropout: keep bit of (query 8u + 4g + t of the block, this lane's key)
     // in bit t of kq[u].  Lane x of each group of four (keys 4 * (kj / 4) + x)
     // draws the bits of query 8u + 4g + x for all four keys; a transpose
@@ -473,7 +506,7 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
     uint32_t kq[4] = {0u, 0u, 0u, 0u};
     f32x16 nd;
     if (DROP) {
-      nd = *reinterpret_cast<const f32x16*>(es + 32 * h + 16 * g);
+      nd = ld_stats16(es + 32 * h + 16 * g);
       const uint32_t x = (uint32_t)(c & 3);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -509,9 +542,10 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
     for (int e = 0; e < DE; ++e)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const int off = (32 * h + 16 * t) * LD + 32 * e + tro;
-        dvt[e] = mfma32x32x16(ld_frag_tr(db + off, LD), pf[t], dvt[e]);
-        dkt[e] = mfma32x32x16(ld_frag_tr(qb + off, LD), sf[t], dkt[e]);
+        const int rb = (32 * h + 16 * t) * D;
+        const int lo = rb + sw.tlo[e], hi = rb + sw.thi[e];
+        dvt[e] = mfma32x32x16(ld_frag_tr2(db + lo, db + hi), pf[t], dvt[e]);
+        dkt[e] = mfma32x32x16(ld_frag_tr2(qb + lo, qb + hi), sf[t], dkt[e]);
       }
   }
 }
@@ -521,18 +555,22 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
     View Q, View K, View V, View dO, const float* __restrict__ LSE,
     const float* __restrict__ Delta, View dK, View dV, Problem pb) {
   constexpr int BN = kKBN;
-  constexpr int LD = D + 8;     // row-major Q / dO tiles
   constexpr int DS = D / 16;
   constexpr int DE = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[2][BM * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Ds[2][BM * LD];
+  // Q and dO tiles of the two buffers, copied in by the DMA (unpadded,
+  // swizzled).  Separate arrays per buffer, and a loop unrolled by two, let
+  // the compiler see that the copy into one buffer does not touch the one
+  // being read, so reads do not wait for the copy.
+  __shared__ __attribute__((aligned(16))) uint16_t QD0[2][BM * D];
+  __shared__ __attribute__((aligned(16))) uint16_t QD1[2][BM * D];
   __shared__ __attribute__((aligned(64))) float Ls[2][BM];
   __shared__ __attribute__((aligned(64))) float Es[2][BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
-  const int tro = tr_rowoff(lane) * LD + tr_coloff(lane);
+  SwzLane<D> sw;
+  sw.init(c, g, tr_rowoff(lane), tr_coloff(lane));
   const int bid = blockIdx.x;
   const int kb = bid / pb.N;  // under plain causal masking, block 0 has the most queries
   const int n = bid % pb.N;
@@ -566,34 +604,33 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
   const int wqhi = k0w < pb.Tk ? queries_hi(min(k0w + 31, pb.Tk - 1), pb) : -1;
   const Span seers = queries_of(kj, pb);  // queries that see this lane's key
 
-  RowStage<BM, D, kThreads> qs, ds;
-  qs.init(tid, LD, Q.st);
-  ds.init(tid, LD, dO.st);
+  TileDMA<BM, D, kThreads> qs, ds;
+  qs.init(tid, Q.st);
+  ds.init(tid, dO.st);
   // Row statistics of the tile: thread t < BM loads query q1 + t.  The loads
   // only issue here; they are turned into -lse * log2(e) and -delta when the
-  // tile is stored, so that the compute in between does not wait for them.
+  // tile is published, so that the compute in between does not wait for them.
   float lraw = 0.0f, draw = 0.0f;
   int qrow = 0;
-  auto load_tile = [&](int qt, int valid) {
+  auto load_tile = [&](int qt, int valid, uint16_t (&qd)[2][BM * D]) {
     const int q1 = qt * BM;
-    qs.load(Qh + (long long)q1 * Q.st, valid);
-    ds.load(Dh + (long long)q1 * dO.st, valid);
+    qs.load(Qh + (long long)q1 * Q.st, valid, qd[0]);
+    ds.load(Dh + (long long)q1 * dO.st, valid, qd[1]);
     qrow = q1 + tid;
     const int cnt = valid < BM ? valid : BM;  // threads tid >= BM read past it: zero
     lraw = load_f32_or_zero(LSE + rows + q1, cnt, tid);
     draw = load_f32_or_zero(Delta + rows + q1, cnt, tid);
   };
-  auto store_tile = [&](int b) {
-    qs.store(Qs[b], LD);
-    ds.store(Ds[b], LD);
+  auto publish_tile = [&](int b) {
     if (tid < BM) {
       const bool live = qrow < pb.Tq && lraw > -INFINITY;  // rows past Tq or seeing no key
       Ls[b][stat_slot(tid)] = live ? -lraw * kLog2e : -INFINITY;
       Es[b][stat_slot(tid)] = -draw;
     }
+    wait_dma();  // this wave's tile copies have landed; the barrier publishes them
   };
-  load_tile(qt0, qt1 >= qt0 ? pb.Tq - qt0 * BM : 0);
-  store_tile(0);
+  load_tile(qt0, qt1 >= qt0 ? pb.Tq - qt0 * BM : 0, QD0);
+  publish_tile(0);
   __syncthreads();
 
   f32x16 dvt[DE], dkt[DE];
@@ -603,31 +640,39 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
     dkt[e] = zero16();
   }
 
-  for (int qt = qt0; qt <= qt1; ++qt) {
-    const int buf = (qt - qt0) & 1;
+  // one tile: compute on buffer `cur` (index b) while the next tile is
+  // copied into buffer `nxt`
+  auto step = [&](int qt, uint16_t (&cur)[2][BM * D], uint16_t (&nxt)[2][BM * D], int b) {
     const bool more = qt < qt1;
-    if (more) load_tile(qt + 1, pb.Tq - (qt + 1) * BM);
+    if (more) load_tile(qt + 1, pb.Tq - (qt + 1) * BM, nxt);
     const int q0 = qt * BM;
     if (q0 + BM - 1 >= wqlo && q0 <= wqhi) {  // some query of the tile sees a key of this wave
       if (needs_mask(q0, q0 + BM - 1, k0w, k0w + 31, pb)) {
         // 32-query blocks of the tile that no key of this wave is seen by
         const int h0 = max(0, (wqlo - q0) >> 5), h1 = min(BM / 32 - 1, (wqhi - q0) >> 5);
-        dkdv_tile<D, BM, true, DROP>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0,
-                                     seers, g, c, tro, kj, n, h0, h1, pb);
+        dkdv_tile<D, BM, true, DROP>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers,
+                                     g, c, sw, kj, n, h0, h1, pb);
       } else {
-        dkdv_tile<D, BM, false, DROP>(Qs[buf], Ds[buf], Ls[buf], Es[buf], kf, vf, dvt, dkt, q0,
-                                      seers, g, c, tro, kj, n, 0, BM / 32 - 1, pb);
+        dkdv_tile<D, BM, false, DROP>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers,
+                                      g, c, sw, kj, n, 0, BM / 32 - 1, pb);
       }
     }
-    if (more) store_tile(buf ^ 1);
+    if (more) publish_tile(b ^ 1);
     __syncthreads();
+  };
+  for (int qt = qt0; qt <= qt1; qt += 2) {
+    step(qt, QD0, QD1, 0);
+    if (qt + 1 <= qt1) step(qt + 1, QD1, QD0, 1);
   }
 
   // the Q / dO tiles are free after the loop's last barrier: 16 rows per wave
-  store_rows<D>(&Qs[0][0] + w * 16 * LD, dkt, pb.scale,
+  constexpr int LD = D + 8;
+  static_assert(2 * 16 * LD <= 2 * BM * D, "two waves' epilogue staging must fit one buffer");
+  uint16_t* stage = (w < 2 ? &QD0[0][0] : &QD1[0][0]) + (w & 1) * 16 * LD;
+  store_rows<D>(stage, dkt, pb.scale,
                 const_cast<uint16_t*>(head_of(dK, n, pb.H)) + (long long)k0w * dK.st, dK.st,
                 pb.Tk - k0w, lane);
-  store_rows<D>(&Qs[0][0] + w * 16 * LD, dvt, 1.0f,
+  store_rows<D>(stage, dvt, 1.0f,
                 const_cast<uint16_t*>(head_of(dV, n, pb.H)) + (long long)k0w * dV.st, dV.st,
                 pb.Tk - k0w, lane);
 }

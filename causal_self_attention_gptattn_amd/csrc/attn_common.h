@@ -284,6 +284,90 @@ struct RowStage {
 };
 
 // ---------------------------------------------------------------------------
+// Global -> LDS copy of a ROWS x D bf16 tile without a register round trip
+// (gfx950 buffer_load_dwordx4 ... lds).  Each lane's 16 bytes land at the
+// lane's position in a contiguous 1024-byte block per wave instruction, so
+// the LDS tile is unpadded (row stride D) and bank conflicts are avoided by
+// a swizzle instead: 16-byte chunk k of row r sits in slot k ^ swz_key(r)
+// of that row.  Each lane picks the global chunk that belongs in its slot.
+// The same descriptor range check as RowStage: rows at or past `valid` read
+// as zero.  The copy completes asynchronously; wait_dma() then a workgroup
+// barrier make it visible.
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+
+// The key depends on r mod 16 and is chosen for the two read patterns of
+// the tiles (64 banks of 4 bytes: a 256-byte window):
+//   ds_read_b128 of one chunk in 16 consecutive rows (16 lanes at a time):
+//     the 16 rows must fill the window once.  D = 64 puts two rows in a
+//     window (row parity picks the half), so the key must take 8 values over
+//     r / 2; D = 128 fills a window per row, so it must take 16 values.
+//   ds_read_b64_tr_b16 of four chunks in 4 consecutive rows 4i..4i+3 (32
+//     lanes at a time): the four 64-byte chunk groups must land in different
+//     quarters of the window, so the key's bits above the chunk-in-group bits
+//     must differ between rows 4i and 4i+2 (D = 64) or among all four (D = 128).
+template <int D>
+__device__ __forceinline__ int swz_key(int row) {
+  static_assert(D == 64 || D == 128, "swizzle defined for rows of 64 or 128 elements");
+  return D == 64 ? ((row & 2) << 1) | ((row >> 2) & 3) : ((row & 3) << 2) | ((row >> 2) & 3);
+}
+
+// Element offset of (row, col) in a swizzled row-major tile of row length D
+// (col a multiple of 4 within one 16-byte chunk, or any col for the chunk's
+// first element).
+template <int D>
+__device__ __forceinline__ int swz(int row, int col) {
+  return row * D + (((col >> 3) ^ swz_key<D>(row)) << 3) + (col & 7);
+}
+
+// ld_frag_tr for a swizzled tile: rows r and r + 8 have different keys, so
+// the two halves take their own addresses.
+__device__ __forceinline__ bf16x8 ld_frag_tr2(const uint16_t* lo, const uint16_t* hi) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lo));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(hi));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, a);
+  const u32x2 h2 = __builtin_bit_cast(u32x2, b);
+  return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
+}
+
+template <int ROWS, int D, int NT>
+struct TileDMA {
+  static constexpr int CPR = D / 8;            // 16-byte chunks per row
+  static constexpr int PER = ROWS * CPR / NT;  // chunks per thread
+  static constexpr int RSTEP = NT / CPR;       // rows between a thread's chunks
+  static_assert((ROWS * CPR) % NT == 0 && NT % CPR == 0 && RSTEP % 16 == 0,
+                "tile must split evenly, and each thread's rows share one swizzle");
+  uint32_t goff;   // byte offset of the thread's first chunk in the global tile
+  uint32_t gstep;  // bytes between the thread's chunks
+  uint32_t rowb;   // bytes between rows in the global tile
+  int wofs;        // element offset of this wave's first slot in the LDS tile
+
+  __device__ __forceinline__ void init(int tid, long long st) {
+    const int row = tid / CPR, slot = tid % CPR;
+    rowb = (uint32_t)(st * 2);
+    goff = (uint32_t)row * rowb + 16u * (uint32_t)(slot ^ swz_key<D>(row));
+    gstep = (uint32_t)RSTEP * rowb;
+    wofs = (tid & ~63) * 8;
+  }
+
+  // src: first element of the tile (uniform); lds: the LDS tile.
+  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int valid,
+                                       uint16_t* lds) const {
+    const int rows = valid <= 0 ? 0 : valid < ROWS ? valid : ROWS;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(src), 0, __builtin_amdgcn_readfirstlane(rows * (int)rowb),
+        kBufferWord3);
+#pragma unroll
+    for (int p = 0; p < PER; ++p)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + wofs + p * NT * 8), 16,
+                                               (int)goff, (int)(p * gstep), 0, 0);
+  }
+};
+
+// Wait for this wave's outstanding global loads, including copies into LDS.
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// ---------------------------------------------------------------------------
 // Epilogue: a wave's 32 x D block of results, held in the MFMA result layout
 // (lane (c, g) holds, for row c, columns 32e + 8u + 4g + i in acc[e][4u + i]),
 // goes to HBM as bf16 through a wave-private LDS region of 16 rows at a time,
