@@ -35,6 +35,11 @@
 //                 are staged row-major in LDS and read transposed for the
 //                 dV/dK products.
 //
+// The tiles a workgroup walks (K/V, or Q/dO) are copied HBM -> LDS by the
+// gfx950 buffer-load-to-LDS path into two alternating buffers, unpadded and
+// swizzled (TileDMA in attn_common.h): the copy of the next tile runs while
+// the current one is computed on, and costs no registers.
+//
 // dQ and dK/dV come from separate kernels, so no result is accumulated with
 // atomics and every output is bitwise reproducible run to run.
 #include "attn_common.h"
@@ -75,10 +80,11 @@ __device__ __forceinline__ bool needs_mask(int i0, int i1, int j0, int j1, const
 // m = -inf; the guards keep -inf from meeting -inf.
 template <int D, bool MASK, bool DROP>
 __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf,
-                                         f32x16* ot, float& m, float& l, int k0, Span seen, int c,
-                                         int g, int tro, int qi, uint32_t n, int h0, int h1,
+                                         f32x16* ot, float& m, float& l, int k0, Span seen, int g,
+                                         const SwzLane<D>& sw, int qi, uint32_t n, int h0, int h1,
                                          const Problem& pb) {
-  constexpr int LD = D + 8, DS = D / 16, DE = D / 32;
+  // K and V tiles: unpadded rows of D, 16-byte chunks swizzled (swz)
+  constexpr int DS = D / 16, DE = D / 32;
   // scheduling hint: interleave the LDS reads with the matrix products so
   // that more than one read is in flight (2-3% measured)
   __builtin_amdgcn_iglp_opt(0);
@@ -86,10 +92,10 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb,
   for (int a = 0; a < 2; ++a) {
     if (MASK && (a < h0 || a > h1)) continue;  // no row of the wave sees these 32 keys
     // S^T = K Q^T for 32 keys: rows = keys, columns = this wave's queries
-    f32x16 st = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 8 * g), qf[0], zero16());
+    f32x16 st = mfma32x32x16(ld_frag16(kb + 32 * a * D + sw.fo[0]), qf[0], zero16());
 #pragma unroll
     for (int s = 1; s < DS; ++s)
-      st = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 16 * s + 8 * g), qf[s], st);
+      st = mfma32x32x16(ld_frag16(kb + 32 * a * D + sw.fo[s]), qf[s], st);
     if (MASK) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -139,9 +145,10 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb,
 #pragma unroll
     for (int e = 0; e < DE; ++e)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        ot[e] = mfma32x32x16(ld_frag_tr(vb + (32 * a + 16 * t) * LD + 32 * e + tro, LD), pf[t],
-                             ot[e]);
+      for (int t = 0; t < 2; ++t) {
+        const uint16_t* vr = vb + (32 * a + 16 * t) * D;
+        ot[e] = mfma32x32x16(ld_frag_tr2(vr + sw.tlo[e], vr + sw.thi[e]), pf[t], ot[e]);
+      }
   }
 }
 
@@ -149,16 +156,21 @@ template <int D, bool DROP>
 __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
     View Q, View K, View V, View O, float* __restrict__ LSE, Problem pb, int nqb) {
   constexpr int BM = kBM, BN = kBN;
-  constexpr int LD = D + 8;     // padded row stride of the LDS tiles
+  constexpr int LD = D + 8;     // row stride of the epilogue staging (padded)
   constexpr int DS = D / 16;    // k-steps of the score product
   constexpr int DE = D / 32;    // 32-row output tiles over the head dim
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * LD];
+  // K and V tiles of the two buffers, copied in by the DMA (unpadded,
+  // swizzled).  Separate arrays per buffer, and a loop unrolled by two, let
+  // the compiler see that the copy into one buffer does not touch the one
+  // being read, so reads do not wait for the copy.
+  __shared__ __attribute__((aligned(16))) uint16_t K0[BN * D], K1[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[BN * D], V1[BN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
-  const int tro = tr_rowoff(lane) * LD + tr_coloff(lane);
+  SwzLane<D> sw;
+  sw.init(c, g, tr_rowoff(lane), tr_coloff(lane));
   const int bid = blockIdx.x;
   const int qb = nqb - 1 - bid / pb.N;  // longest query blocks first
   const int n = bid % pb.N;
@@ -189,17 +201,17 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
   // keys some row of this wave sees (32-key halves outside are skipped)
   const int wklo = keys_lo(q0w, pb), wkhi = keys_hi(wlast, pb);
 
-  RowStage<BN, D, kThreads> ks, vs;
-  ks.init(tid, LD, K.st);
-  vs.init(tid, LD, V.st);
-  {  // first tile (reads nothing when the workgroup sees no key)
-    const int k1 = ws.t0 * BN;
-    const int valid = ws.t1 >= ws.t0 ? pb.Tk - k1 : 0;
-    ks.load(Kh + (long long)k1 * K.st, valid);
-    vs.load(Vh + (long long)k1 * V.st, valid);
-    ks.store(Ks[0], LD);
-    vs.store(Vs[0], LD);
-  }
+  TileDMA<BN, D, kThreads> ks, vs;
+  ks.init(tid, K.st);
+  vs.init(tid, V.st);
+  auto load_tile = [&](int kt, int valid, uint16_t* kd, uint16_t* vd) {
+    const int k1 = kt * BN;
+    ks.load(Kh + (long long)k1 * K.st, valid, kd);
+    vs.load(Vh + (long long)k1 * V.st, valid, vd);
+  };
+  // first tile (reads nothing when the workgroup sees no key)
+  load_tile(ws.t0, ws.t1 >= ws.t0 ? pb.Tk - ws.t0 * BN : 0, K0, V0);
+  wait_dma();
   __syncthreads();
 
   f32x16 ot[DE];
@@ -207,29 +219,25 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
   for (int e = 0; e < DE; ++e) ot[e] = zero16();
   float m = -INFINITY, l = 0.0f;
 
-  for (int kt = ws.t0; kt <= ws.t1; ++kt) {
-    const int buf = (kt - ws.t0) & 1;
+  // one tile: compute on (kc, vc) while the next tile is copied into (kn, vn)
+  auto step = [&](int kt, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
     const bool more = kt < ws.t1;
-    if (more) {
-      const int k1 = (kt + 1) * BN;
-      ks.load(Kh + (long long)k1 * K.st, pb.Tk - k1);
-      vs.load(Vh + (long long)k1 * V.st, pb.Tk - k1);
-    }
+    if (more) load_tile(kt + 1, pb.Tk - (kt + 1) * BN, kn, vn);
     if (kt >= wv.t0 && kt <= wv.t1) {
       const int k0 = kt * BN;
       if (needs_mask(q0w, wlast, k0, k0 + BN - 1, pb)) {
-        fwd_tile<D, true, DROP>(Ks[buf], Vs[buf], qf, ot, m, l, k0, seen, c, g, tro, qi, n,
+        fwd_tile<D, true, DROP>(kc, vc, qf, ot, m, l, k0, seen, g, sw, qi, n,
                                 k0 + 31 < wklo ? 1 : 0, k0 + 32 > wkhi ? 0 : 1, pb);
       } else {
-        fwd_tile<D, false, DROP>(Ks[buf], Vs[buf], qf, ot, m, l, k0, seen, c, g, tro, qi, n, 0, 1,
-                                 pb);
+        fwd_tile<D, false, DROP>(kc, vc, qf, ot, m, l, k0, seen, g, sw, qi, n, 0, 1, pb);
       }
     }
-    if (more) {
-      ks.store(Ks[buf ^ 1], LD);
-      vs.store(Vs[buf ^ 1], LD);
-    }
+    if (more) wait_dma();  // this wave's copies have landed; the barrier publishes them
     __syncthreads();
+  };
+  for (int kt = ws.t0; kt <= ws.t1; kt += 2) {
+    step(kt, K0, V0, K1, V1);
+    if (kt + 1 <= ws.t1) step(kt + 1, K1, V1, K0, V0);
   }
 
   const float lt = half_sum(l);
@@ -237,7 +245,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
   if (qi < pb.Tq && g == 0)
     LSE[(long long)n * pb.Tq + qi] = lt > 0.0f ? (m + log2f(lt)) * kLn2 : -INFINITY;
   // the K tiles are free after the loop's last barrier: 16 rows per wave
-  store_rows<D>(&Ks[0][0] + w * 16 * LD, ot, inv,
+  static_assert(2 * 16 * LD <= BN * D, "two waves' epilogue staging must fit one K tile");
+  store_rows<D>((w < 2 ? K0 : K1) + (w & 1) * 16 * LD, ot, inv,
                 const_cast<uint16_t*>(head_of(O, n, pb.H)) + (long long)q0w * O.st, O.st,
                 pb.Tq - q0w, lane);
 }
@@ -253,9 +262,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
 template <int D, bool MASK, bool DROP>
 __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf,
                                         const bf16x8* df, const f32x16& nd, f32x16* acc, int k0,
-                                        Span seen, int c, int g, int tro, float nl, int qi,
+                                        Span seen, int g, const SwzLane<D>& sw, float nl, int qi,
                                         uint32_t n, int h0, int h1, const Problem& pb) {
-  constexpr int LD = D + 8, DS = D / 16, DE = D / 32;
+  // K and V tiles: unpadded rows of D, 16-byte chunks swizzled (swz)
+  constexpr int DS = D / 16, DE = D / 32;
   // scheduling hint: interleave the LDS reads with the matrix products so
   // that more than one read is in flight (2-3% measured)
   __builtin_amdgcn_iglp_opt(0);
@@ -267,12 +277,12 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     if (MASK && (a < h0 || a > h1)) continue;  // no row of the wave sees these 32 keys
-    st[a] = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 8 * g), qf[0], zero16());
-    dp[a] = mfma32x32x16(ld_frag16(vb + (32 * a + c) * LD + 8 * g), df[0], nd);
+    st[a] = mfma32x32x16(ld_frag16(kb + 32 * a * D + sw.fo[0]), qf[0], zero16());
+    dp[a] = mfma32x32x16(ld_frag16(vb + 32 * a * D + sw.fo[0]), df[0], nd);
 #pragma unroll
     for (int s = 1; s < DS; ++s) {
-      st[a] = mfma32x32x16(ld_frag16(kb + (32 * a + c) * LD + 16 * s + 8 * g), qf[s], st[a]);
-      dp[a] = mfma32x32x16(ld_frag16(vb + (32 * a + c) * LD + 16 * s + 8 * g), df[s], dp[a]);
+      st[a] = mfma32x32x16(ld_frag16(kb + 32 * a * D + sw.fo[s]), qf[s], st[a]);
+      dp[a] = mfma32x32x16(ld_frag16(vb + 32 * a * D + sw.fo[s]), df[s], dp[a]);
     }
   }
 #pragma unroll
@@ -312,9 +322,10 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
 #pragma unroll
     for (int e = 0; e < DE; ++e)
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-        acc[e] = mfma32x32x16(ld_frag_tr(kb + (32 * a + 16 * t) * LD + 32 * e + tro, LD), sf[t],
-                              acc[e]);
+      for (int t = 0; t < 2; ++t) {
+        const uint16_t* kr = kb + (32 * a + 16 * t) * D;
+        acc[e] = mfma32x32x16(ld_frag_tr2(kr + sw.tlo[e], kr + sw.thi[e]), sf[t], acc[e]);
+      }
   }
 }
 
@@ -326,13 +337,18 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dq(
   constexpr int LD = D + 8;
   constexpr int DS = D / 16;
   constexpr int DE = D / 32;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2][BN * LD];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2][BN * LD];
+  // K and V tiles of the two buffers, copied in by the DMA (unpadded,
+  // swizzled).  Separate arrays per buffer, and a loop unrolled by two, let
+  // the compiler see that the copy into one buffer does not touch the one
+  // being read, so reads do not wait for the copy.
+  __shared__ __attribute__((aligned(16))) uint16_t K0[BN * D], K1[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[BN * D], V1[BN * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, g = lane >> 5;
-  const int tro = tr_rowoff(lane) * LD + tr_coloff(lane);
+  SwzLane<D> sw;
+  sw.init(c, g, tr_rowoff(lane), tr_coloff(lane));
   const int bid = blockIdx.x;
   const int qb = nqb - 1 - bid / pb.N;
   const int n = bid % pb.N;
@@ -381,49 +397,47 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dq(
   // keys some row of this wave sees (32-key halves outside are skipped)
   const int wklo = keys_lo(q0w, pb), wkhi = keys_hi(wlast, pb);
 
-  RowStage<BN, D, kThreads> ks, vs;
-  ks.init(tid, LD, K.st);
-  vs.init(tid, LD, V.st);
-  {  // first tile (reads nothing when the workgroup sees no key)
-    const int k1 = ws.t0 * BN;
-    const int valid = ws.t1 >= ws.t0 ? pb.Tk - k1 : 0;
-    ks.load(Kh + (long long)k1 * K.st, valid);
-    vs.load(Vh + (long long)k1 * V.st, valid);
-    ks.store(Ks[0], LD);
-    vs.store(Vs[0], LD);
-  }
+  TileDMA<BN, D, kThreads> ks, vs;
+  ks.init(tid, K.st);
+  vs.init(tid, V.st);
+  auto load_tile = [&](int kt, int valid, uint16_t* kd, uint16_t* vd) {
+    const int k1 = kt * BN;
+    ks.load(Kh + (long long)k1 * K.st, valid, kd);
+    vs.load(Vh + (long long)k1 * V.st, valid, vd);
+  };
+  // first tile (reads nothing when the workgroup sees no key)
+  load_tile(ws.t0, ws.t1 >= ws.t0 ? pb.Tk - ws.t0 * BN : 0, K0, V0);
+  wait_dma();
   __syncthreads();
 
   f32x16 acc[DE];
 #pragma unroll
   for (int e = 0; e < DE; ++e) acc[e] = zero16();
 
-  for (int kt = ws.t0; kt <= ws.t1; ++kt) {
-    const int buf = (kt - ws.t0) & 1;
+  // one tile: compute on (kc, vc) while the next tile is copied into (kn, vn)
+  auto step = [&](int kt, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
     const bool more = kt < ws.t1;
-    if (more) {
-      const int k1 = (kt + 1) * BN;
-      ks.load(Kh + (long long)k1 * K.st, pb.Tk - k1);
-      vs.load(Vh + (long long)k1 * V.st, pb.Tk - k1);
-    }
+    if (more) load_tile(kt + 1, pb.Tk - (kt + 1) * BN, kn, vn);
     if (kt >= wv.t0 && kt <= wv.t1) {
       const int k0 = kt * BN;
       if (needs_mask(q0w, wlast, k0, k0 + BN - 1, pb)) {
-        dq_tile<D, true, DROP>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, seen, c, g, tro, nl, qi, n,
+        dq_tile<D, true, DROP>(kc, vc, qf, df, nd, acc, k0, seen, g, sw, nl, qi, n,
                                k0 + 31 < wklo ? 1 : 0, k0 + 32 > wkhi ? 0 : 1, pb);
       } else {
-        dq_tile<D, false, DROP>(Ks[buf], Vs[buf], qf, df, nd, acc, k0, seen, c, g, tro, nl, qi, n,
-                                0, 1, pb);
+        dq_tile<D, false, DROP>(kc, vc, qf, df, nd, acc, k0, seen, g, sw, nl, qi, n, 0, 1, pb);
       }
     }
-    if (more) {
-      ks.store(Ks[buf ^ 1], LD);
-      vs.store(Vs[buf ^ 1], LD);
-    }
+    if (more) wait_dma();  // this wave's copies have landed; the barrier publishes them
     __syncthreads();
+  };
+  for (int kt = ws.t0; kt <= ws.t1; kt += 2) {
+    step(kt, K0, V0, K1, V1);
+    if (kt + 1 <= ws.t1) step(kt + 1, K1, V1, K0, V0);
   }
 
-  store_rows<D>(&Ks[0][0] + w * 16 * LD, acc, pb.scale,
+  // the K tiles are free after the loop's last barrier: 16 rows per wave
+  static_assert(2 * 16 * LD <= BN * D, "two waves' epilogue staging must fit one K tile");
+  store_rows<D>((w < 2 ? K0 : K1) + (w & 1) * 16 * LD, acc, pb.scale,
                 const_cast<uint16_t*>(head_of(dQ, n, pb.H)) + (long long)q0w * dQ.st, dQ.st,
                 pb.Tq - q0w, lane);
 }
@@ -452,25 +466,6 @@ __device__ __forceinline__ f32x16 ld_stats16(const float* p) {
   return f32x16{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3],
                 c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
 }
-
-// This lane's element offsets into a swizzled Q / dO tile for the reads of
-// dkdv_tile, relative to the first row of a 32-query block.  The swizzle key
-// repeats every 16 rows, so the offsets are the same for every block and the
-// block's position becomes an immediate offset of the read instruction.
-template <int D>
-struct SwzLane {
-  int fo[D / 16];          // row c, chunk 2s + g: fragments of Q and dO
-  int tlo[D / 32], thi[D / 32];  // rows trr and trr + 8, columns 32e + trc: transposed
-  __device__ __forceinline__ void init(int c, int g, int trr, int trc) {
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) fo[s] = swz<D>(c, 16 * s + 8 * g);
-#pragma unroll
-    for (int e = 0; e < D / 32; ++e) {
-      tlo[e] = swz<D>(trr, 32 * e + trc);
-      thi[e] = swz<D>(trr + 8, 32 * e + trc);
-    }
-  }
-};
 
 // One BM-query tile for one wave (32 keys, one per lane column c).  ls/es
 // hold -lse * log2(e) (-inf for rows that see no key or lie past Tq) and

@@ -217,18 +217,12 @@ __device__ __forceinline__ uint32_t quad_lane(uint32_t v) {
 }
 
 // ---------------------------------------------------------------------------
-// Global -> LDS staging of a ROWS x D bf16 tile (rows `st` elements apart in
-// HBM, st >= D, D contiguous) into a row-major LDS tile with leading
-// dimension ld.  Thread t of NT moves 16-byte chunks t, t + NT, ...; eight
-// consecutive threads cover one 128-byte row segment, so each wave's loads
-// and stores are contiguous.
-//
-// The loads are buffer loads through a descriptor whose range ends at the
-// last row that exists: the hardware returns zero for the chunks of rows at
-// or past `valid`, so a ragged last tile needs no branch and no select, and
-// the loads of a tile issue back to back.  Because st >= D, every chunk of
-// a row r < valid lies below valid * st elements and every chunk of a row
-// r >= valid lies at or above it.
+// Range-checked loads.  Global reads of tiles and row statistics go through
+// a buffer descriptor whose range ends at the last row that exists: the
+// hardware returns zero for reads at or past the end, so a ragged last tile
+// needs no branch and no select, and the loads of a tile issue back to back.
+// Because st >= D, every chunk of a row r < valid lies below valid * st
+// elements and every chunk of a row r >= valid lies at or above it.
 // ---------------------------------------------------------------------------
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer access (gfx9 family)
 
@@ -243,55 +237,17 @@ __device__ __forceinline__ float load_f32_or_zero(const float* base, int n, int 
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, i * 4, 0, 0));
 }
 
-template <int ROWS, int D, int NT>
-struct RowStage {
-  static constexpr int CPR = D / 8;            // 16-byte chunks per row
-  static constexpr int PER = ROWS * CPR / NT;  // chunks per thread
-  static constexpr int RSTEP = NT / CPR;       // rows between a thread's chunks
-  static_assert((ROWS * CPR) % NT == 0 && NT % CPR == 0, "tile must split evenly");
-  u32x4 r[PER];
-  uint32_t goff;   // byte offset of the thread's first chunk in the global tile
-  uint32_t gstep;  // bytes between the thread's chunks (uniform: a scalar offset)
-  uint32_t rowb;   // bytes between rows in the global tile
-  uint32_t loff;   // element offset of the thread's first chunk in the LDS tile
-
-  __device__ __forceinline__ void init(int tid, int ld, long long st) {
-    const int row = tid / CPR;
-    rowb = (uint32_t)(st * 2);
-    goff = (uint32_t)row * rowb + 16u * (uint32_t)(tid % CPR);
-    gstep = (uint32_t)RSTEP * rowb;
-    loff = (uint32_t)(row * ld + 8 * (tid % CPR));
-  }
-
-  // src: first element of the tile (uniform across the workgroup); rows at or
-  // past `valid` read as zero, and with valid <= 0 nothing is read at all.
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int valid) {
-    const int rows = valid <= 0 ? 0 : valid < ROWS ? valid : ROWS;
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(src), 0, __builtin_amdgcn_readfirstlane(rows * (int)rowb),
-        kBufferWord3);
-#pragma unroll
-    for (int p = 0; p < PER; ++p)
-      r[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                           rs, (int)goff, (int)(p * gstep), 0));
-  }
-
-  __device__ __forceinline__ void store(uint16_t* dst, int ld) const {
-#pragma unroll
-    for (int p = 0; p < PER; ++p)
-      *reinterpret_cast<u32x4*>(dst + loff + p * RSTEP * ld) = r[p];
-  }
-};
-
 // ---------------------------------------------------------------------------
-// Global -> LDS copy of a ROWS x D bf16 tile without a register round trip
-// (gfx950 buffer_load_dwordx4 ... lds).  Each lane's 16 bytes land at the
-// lane's position in a contiguous 1024-byte block per wave instruction, so
-// the LDS tile is unpadded (row stride D) and bank conflicts are avoided by
-// a swizzle instead: 16-byte chunk k of row r sits in slot k ^ swz_key(r)
-// of that row.  Each lane picks the global chunk that belongs in its slot.
-// The same descriptor range check as RowStage: rows at or past `valid` read
-// as zero.  The copy completes asynchronously; wait_dma() then a workgroup
+// Global -> LDS copy of a ROWS x D bf16 tile (rows `st` elements apart in
+// HBM, st >= D, D contiguous) without a register round trip (gfx950
+// buffer_load_dwordx4 ... lds).  Thread t of NT moves 16-byte chunks t,
+// t + NT, ...  Each lane's 16 bytes land at the lane's position in a
+// contiguous 1024-byte block per wave instruction, so the LDS tile is
+// unpadded (row stride D) and bank conflicts are avoided by a swizzle
+// instead: 16-byte chunk k of row r sits in slot k ^ swz_key(r) of that row.
+// Each lane picks the global chunk that belongs in its slot, so a wave still
+// reads whole rows.  Rows at or past `valid` read as zero (range check
+// above).  The copy completes asynchronously; wait_dma() then a workgroup
 // barrier make it visible.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
@@ -361,6 +317,27 @@ struct TileDMA {
     for (int p = 0; p < PER; ++p)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(lds + wofs + p * NT * 8), 16,
                                                (int)goff, (int)(p * gstep), 0, 0);
+  }
+};
+
+// This lane's element offsets into a swizzled tile for the two MFMA operand
+// reads, relative to the first row of a 32-row block: the 16-byte fragment
+// of row c (ld_frag16) and the transposed 8-byte pieces of rows trr and
+// trr + 8 (ld_frag_tr2).  The swizzle key repeats every 16 rows, so the
+// offsets are the same for every block and the block's position becomes an
+// immediate offset of the read instruction.
+template <int D>
+struct SwzLane {
+  int fo[D / 16];                // row c, chunk 2s + g
+  int tlo[D / 32], thi[D / 32];  // rows trr and trr + 8, columns 32e + trc: transposed
+  __device__ __forceinline__ void init(int c, int g, int trr, int trc) {
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) fo[s] = swz<D>(c, 16 * s + 8 * g);
+#pragma unroll
+    for (int e = 0; e < D / 32; ++e) {
+      tlo[e] = swz<D>(trr, 32 * e + trc);
+      thi[e] = swz<D>(trr + 8, 32 * e + trc);
+    }
   }
 };
 
