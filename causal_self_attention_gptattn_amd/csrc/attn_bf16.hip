@@ -180,17 +180,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 1) void attn_fwd(
   const int q0w = q0 + 32 * w;
   const int qi = q0w + c;
 
-  bf16x8 qf[DS];
+  bf16x8 qf[DS];  // this lane's query row (zero past Tq)
   {
-    const uint16_t* qr = head_of(Q, n, pb.H) + (long long)qi * Q.st;
+    RowBlock qr;
+    qr.init(head_of(Q, n, pb.H) + (long long)q0w * Q.st, pb.Tq - q0w, Q.st, c);
 #pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      if (qi < pb.Tq) {
-        qf[s] = ld_frag16(qr + 16 * s + 8 * g);
-      } else {
-        qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-      }
-    }
+    for (int s = 0; s < DS; ++s) qf[s] = __builtin_bit_cast(bf16x8, qr.load(16 * s + 8 * g));
   }
 
   // key tiles seen by the workgroup's rows, and by this wave's rows
@@ -359,37 +354,6 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dq(
   const int qi = q0w + c;
   const long long row = (long long)n * pb.Tq + qi;
 
-  bf16x8 qf[DS], df[DS];
-  float dpart = 0.0f;
-  {
-    const uint16_t* qr = head_of(Q, n, pb.H) + (long long)qi * Q.st;
-    const uint16_t* dr = head_of(dO, n, pb.H) + (long long)qi * dO.st;
-    const uint16_t* orr = head_of(O, n, pb.H) + (long long)qi * O.st;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      if (qi < pb.Tq) {
-        const int off = 16 * s + 8 * g;
-        qf[s] = ld_frag16(qr + off);
-        const u32x4 dou = *reinterpret_cast<const u32x4*>(dr + off);
-        const u32x4 ou = *reinterpret_cast<const u32x4*>(orr + off);
-        df[s] = __builtin_bit_cast(bf16x8, dou);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          dpart += bf16_lo(dou[j]) * bf16_lo(ou[j]) + bf16_hi(dou[j]) * bf16_hi(ou[j]);
-      } else {
-        qf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        df[s] = qf[s];
-      }
-    }
-  }
-  const float delta = half_sum(dpart);
-  const float lse = qi < pb.Tq ? LSE[row] : -INFINITY;
-  const float nl = lse > -INFINITY ? -lse * kLog2e : -INFINITY;
-  if (qi < pb.Tq && g == 0) Delta[row] = delta;
-  f32x16 nd;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) nd[r] = -delta;
-
   const TileSpan ws = key_tiles(q0, q0 + BM - 1, pb, BN);
   const TileSpan wv = key_tiles(q0w, q0w + 31, pb, BN);
   const int wlast = min(q0w + 31, pb.Tq - 1);
@@ -405,8 +369,40 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dq(
     ks.load(Kh + (long long)k1 * K.st, valid, kd);
     vs.load(Vh + (long long)k1 * V.st, valid, vd);
   };
-  // first tile (reads nothing when the workgroup sees no key)
+  // first tile (reads nothing when the workgroup sees no key), issued
+  // before the row loads below so that the two latencies overlap
   load_tile(ws.t0, ws.t1 >= ws.t0 ? pb.Tk - ws.t0 * BN : 0, K0, V0);
+
+  const float lse = qi < pb.Tq ? load_f32_or_zero(LSE + (row - c), pb.Tq - q0w, c) : -INFINITY;
+  bf16x8 qf[DS], df[DS];  // this lane's query rows of Q and dO (zero past Tq)
+  float dpart = 0.0f;
+  {
+    RowBlock qr, dr, orr;
+    qr.init(head_of(Q, n, pb.H) + (long long)q0w * Q.st, pb.Tq - q0w, Q.st, c);
+    dr.init(head_of(dO, n, pb.H) + (long long)q0w * dO.st, pb.Tq - q0w, dO.st, c);
+    orr.init(head_of(O, n, pb.H) + (long long)q0w * O.st, pb.Tq - q0w, O.st, c);
+    u32x4 ou[DS];
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      qf[s] = __builtin_bit_cast(bf16x8, qr.load(16 * s + 8 * g));
+      df[s] = __builtin_bit_cast(bf16x8, dr.load(16 * s + 8 * g));
+      ou[s] = orr.load(16 * s + 8 * g);
+    }
+#pragma unroll
+    for (int s = 0; s < DS; ++s) {
+      const u32x4 du = __builtin_bit_cast(u32x4, df[s]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dpart += bf16_lo(du[j]) * bf16_lo(ou[s][j]) + bf16_hi(du[j]) * bf16_hi(ou[s][j]);
+    }
+  }
+  const float delta = half_sum(dpart);
+  const float nl = lse > -INFINITY ? -lse * kLog2e : -INFINITY;
+  if (qi < pb.Tq && g == 0) Delta[row] = delta;
+  f32x16 nd;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) nd[r] = -delta;
+
   wait_dma();
   __syncthreads();
 
@@ -585,19 +581,15 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
   const int k0w = k0 + 32 * w;
   const int kj = k0w + c;
 
-  bf16x8 kf[DS], vf[DS];
+  bf16x8 kf[DS], vf[DS];  // this lane's key rows of K and V (zero past Tk)
   {
-    const uint16_t* kr = head_of(K, n, pb.H) + (long long)kj * K.st;
-    const uint16_t* vr = head_of(V, n, pb.H) + (long long)kj * V.st;
+    RowBlock kr, vr;
+    kr.init(head_of(K, n, pb.H) + (long long)k0w * K.st, pb.Tk - k0w, K.st, c);
+    vr.init(head_of(V, n, pb.H) + (long long)k0w * V.st, pb.Tk - k0w, V.st, c);
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
-      if (kj < pb.Tk) {
-        kf[s] = ld_frag16(kr + 16 * s + 8 * g);
-        vf[s] = ld_frag16(vr + 16 * s + 8 * g);
-      } else {
-        kf[s] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-        vf[s] = kf[s];
-      }
+      kf[s] = __builtin_bit_cast(bf16x8, kr.load(16 * s + 8 * g));
+      vf[s] = __builtin_bit_cast(bf16x8, vr.load(16 * s + 8 * g));
     }
   }
 

@@ -237,6 +237,29 @@ __device__ __forceinline__ float load_f32_or_zero(const float* base, int n, int 
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, i * 4, 0, 0));
 }
 
+// A wave's block of 32 rows of a bf16 matrix (rows `st` elements apart,
+// st >= D): 16-byte pieces of row r (0 <= r < 32, this lane's row) through a
+// range-checked descriptor, zero for rows at or past `valid` (no memory
+// access), so that the loads need no branch and issue back to back.  base
+// (the block's first row) and valid are uniform across the wave.
+struct RowBlock {
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t roff;  // byte offset of this lane's row
+
+  __device__ __forceinline__ void init(const uint16_t* base, int valid, long long st, int r) {
+    const int rows = valid <= 0 ? 0 : valid < 32 ? valid : 32;
+    rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), 0,
+                                           __builtin_amdgcn_readfirstlane(rows * (int)(st * 2)),
+                                           kBufferWord3);
+    roff = (uint32_t)r * (uint32_t)(st * 2);
+  }
+  // elements col .. col + 7 of this lane's row
+  __device__ __forceinline__ u32x4 load(int col) const {
+    return __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(roff + 2u * (uint32_t)col), 0, 0));
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Global -> LDS copy of a ROWS x D bf16 tile (rows `st` elements apart in
 // HBM, st >= D, D contiguous) without a register round trip (gfx950
