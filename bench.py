@@ -11,7 +11,11 @@ triangle including the diagonal).  Score recomputation in the backward is
 implementation work and is not counted.
 
 Prints one JSON line.  Per-kernel durations come from HIP events recorded on
-the launch stream around every launch of the timed steps.
+the launch stream around every launch of a separate pass of steps.  Each
+event record costs the stream a few microseconds, so the timed steps carry
+only two per step, around the dominant kernel: its duration for the roofline
+is measured live over the timed steps, and the step-to-step intervals of the
+second event give the per-step spread.
 
 The line also carries "variants": the strided entry points timed the same
 way (HIP events around each step) on the same head shape -- q, k, v read in
@@ -306,14 +310,18 @@ def main():
 
     launches = [("attn_fwd", fwd), ("attn_bwd_dq", bdq), ("attn_bwd_dkdv", bdkdv)]
 
-    def step(events=None):
+    def step(events=None, around=None):
+        """One step.  events: one event per launch boundary (len(launches) + 1),
+        or with `around` = i a pair recorded just before and after launch i."""
         for i, (name, fn) in enumerate(launches):
-            if events is not None:
-                events[i].record(stream)
+            if events is not None and (around is None or around == i):
+                events[0 if around is not None else i].record(stream)
             rc = fn()
             if rc != 0:
                 raise RuntimeError("%s: %s" % (name, G.status_string(rc)))
-        if events is not None:
+            if events is not None and around == i:
+                events[1].record(stream)
+        if events is not None and around is None:
             events[len(launches)].record(stream)
 
     print("bench: warmup %d steps" % args.warmup, file=sys.stderr, flush=True)
@@ -321,23 +329,33 @@ def main():
         step()
     torch.cuda.synchronize(dev)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
+    # per-kernel durations: a pass with an event at every launch boundary
+    print("bench: per-kernel pass %d steps" % args.steps, file=sys.stderr, flush=True)
+    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
            for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(pev[i])
+    torch.cuda.synchronize(dev)
+    per_kernel_ms = {name: 0.0 for name, _ in launches}
+    for e in pev:
+        for i, (name, _) in enumerate(launches):
+            per_kernel_ms[name] += e[i].elapsed_time(e[i + 1])
+    per_kernel_ms = {k_: t / args.steps for k_, t in per_kernel_ms.items()}
+    dom = max(per_kernel_ms, key=per_kernel_ms.get)
+    dom_i = [name for name, _ in launches].index(dom)
+
+    # timed steps: two events per step, around the dominant kernel
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(evs[i])
+        step(evs[i], around=dom_i)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
 
-    per_kernel_ms = {name: 0.0 for name, _ in launches}
-    step_ms = []
-    for e in evs:
-        for i, (name, _) in enumerate(launches):
-            per_kernel_ms[name] += e[i].elapsed_time(e[i + 1])
-        step_ms.append(e[0].elapsed_time(e[len(launches)]))
-    per_kernel_ms = {k_: t / args.steps for k_, t in per_kernel_ms.items()}
+    dom_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    step_ms = [evs[i - 1][1].elapsed_time(evs[i][1]) for i in range(1, args.steps)]
     q1, med, q3 = (float(x) for x in np.percentile(step_ms, [25, 50, 75]))
 
     # Cold-cache steps: overwrite a 1 GiB buffer before each (outside events).
@@ -359,9 +377,7 @@ def main():
     ms = wall * 1e3 / args.steps
     value = flops / (wall / args.steps) / 1e12
     table = kernel_table(N, T, D)
-    dom = max(per_kernel_ms, key=per_kernel_ms.get)
-    dom_s = per_kernel_ms[dom] * 1e-3
-    achieved = table[dom]["flops"] / dom_s / 1e12
+    achieved = table[dom]["flops"] / (dom_ms * 1e-3) / 1e12
     kernels = {}
     for name, t_ms in per_kernel_ms.items():
         tf = table[name]["flops"] / (t_ms * 1e-3) / 1e12
@@ -414,6 +430,7 @@ def main():
         "cold_cache_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
         "roofline": {
             "kernel": dom,
+            "kernel_ms": round(dom_ms, 5),
             "bound": "mfma",
             "achieved": round(achieved, 2),
             "peak": PEAK_BF16_TFLOPS,
