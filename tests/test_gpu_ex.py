@@ -204,3 +204,41 @@ def test_plain_case_equals_dense_entry_points():
     torch.cuda.synchronize()
     for name, t in zip(("o", "lse", "dq", "dk", "dv"), (o, lse) + tuple(g)):
         assert np.array_equal(a[name], to64(t)), name
+
+
+def wide_rows(t, st, dev):
+    """Copy [B, H, T, D] into a buffer whose rows are `st` elements apart,
+    heads side by side in a row; returns the [B, H, T, D] view."""
+    B, H, T, D = t.shape
+    assert B == 1 and H * D <= st
+    buf = torch.zeros(T * st, dtype=t.dtype, device=dev)
+    view = buf.as_strided((B, H, T, D), (T * st, D, st, 1))
+    view.copy_(t.to(dev))
+    return view
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("f32", 32)])
+def test_max_row_stride(dtype, D):
+    """Row stride at the largest value the calls accept (2^23 elements): the
+    range-checked row loads and tile copies use 32-bit byte offsets within a
+    tile, which must hold at that stride.  Results equal the dense path."""
+    dev = need_gpu()
+    st = 1 << 23
+    B, H, T = 1, 2, 70
+    say("max row stride", dtype, D, st)
+    inp = W.make_inputs(B, H, T, D, dtype, seed=31, recipe="projection" if dtype == "bf16" else "iid")
+    q, k, v, do = (wide_rows(inp[n], st, dev) for n in ("q", "k", "v", "do"))
+    o = wide_rows(torch.zeros_like(inp["q"]), st, dev)
+    dq, dk, dv = (wide_rows(torch.zeros_like(inp["q"]), st, dev) for _ in range(3))
+    assert q.stride(2) == st
+    o, lse = G.fwd_ex(q, k, v, inp["scale"], out=o)
+    G.bwd_ex(q, k, v, o, do, lse, inp["scale"], dq=dq, dk=dk, dv=dv)
+    qc, kc, vc, dc = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    o2, lse2 = G.fwd(qc, kc, vc, inp["scale"])
+    g2 = G.bwd(qc, kc, vc, o2, dc, lse2, inp["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(o.contiguous(), o2) and torch.equal(lse, lse2)
+    for a, b in zip((dq, dk, dv), g2):
+        assert torch.equal(a.contiguous(), b)
+    got = {"o": to64(o), "lse": to64(lse), "dq": to64(dq), "dk": to64(dk), "dv": to64(dv)}
+    compare(got, run_oracle(inp), dtype, label="row stride 2^23 %s D=%d" % (dtype, D))
