@@ -1,6 +1,7 @@
 // Shared device-side building blocks for the gfx950 attention kernels:
-// vector types, the bf16 matrix-core product, conversions and the
-// global -> LDS tile stager.
+// vector types, the bf16 matrix-core product, conversions, range-checked
+// row loads, the HBM -> LDS tile copy with its swizzled layout, and the
+// row-wise epilogue store.
 //
 // Matrix-core product used throughout: v_mfma_f32_32x32x16_bf16, one wave
 // (64 lanes) computes D[32x32] += A[32x16] * B[16x32].  With lane = 32*g + c
