@@ -57,8 +57,47 @@ def run_oracle(inp, heads=None, offset=0, window=0):
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
 
-def compare(got, ref, dtype, heads=None, label=""):
-    """Assert parity on all heads or on the listed (b, h) heads."""
+def rounding_bound(inp, offset=0, window=0, dropout=0.0, seed=0, stream=0):
+    """Per element, a first-order bound (unit round-off u = 2^-8 per rounding)
+    on what the bf16 path's storage roundings can move each output by: the
+    (dropped-out) weights rounded before P V and P^T dO, dS rounded before
+    dS K and dS^T Q, the row term delta formed from the bf16-stored O, and
+    every output rounded once.  Float64, oracle side.  The sweep and dropout
+    tests draw iid N(0, 1) data (gradients 100x the workloads', whose dO is
+    N(0, 0.01)) and amplify kept weights by 1 / (1 - p); there the storage
+    floor alone can exceed the fixed 2e-2, and this bound is the yardstick.
+    The bound is worst-case: measured errors sit well inside it."""
+    from oracle import philox
+    u = 2.0 ** -8
+    q, k, v, do = (inp[n].to(torch.float64).numpy() for n in ("q", "k", "v", "do"))
+    sc = float(np.float32(inp["scale"]))
+    B, H, Tq, _ = q.shape
+    out = {n: np.zeros_like(x) for n, x in (("o", q), ("dq", q), ("dk", k), ("dv", v))}
+    for b in range(B):
+        for h in range(H):
+            qh, kh, vh, dh = q[b, h], k[b, h], v[b, h], do[b, h]
+            p = A.probabilities(qh, kh, inp["scale"], offset, window)
+            f = 1.0
+            if dropout > 0:
+                keep = philox.keep_mask(b * H + h, Tq, kh.shape[0], dropout, seed, stream)
+                f = keep.astype(np.float64) / (1.0 - float(np.float32(dropout)))
+            pd = p * f
+            o = pd @ vh
+            ds = p * ((dh @ vh.T) * f - (dh * o).sum(axis=1, keepdims=True))
+            derr = u * (np.abs(dh) * np.abs(o)).sum(axis=1, keepdims=True)
+            out["o"][b, h] = u * (np.abs(pd) @ np.abs(vh)) + u * np.abs(o)
+            out["dv"][b, h] = u * (np.abs(pd).T @ np.abs(dh)) + u * np.abs(pd.T @ dh)
+            out["dq"][b, h] = (u * sc * (np.abs(ds) @ np.abs(kh)) + sc * derr * (p @ np.abs(kh))
+                               + u * np.abs(sc * ds @ kh))
+            out["dk"][b, h] = (u * sc * (np.abs(ds).T @ np.abs(qh)) + sc * (p * derr).T @ np.abs(qh)
+                               + u * np.abs(sc * ds.T @ qh))
+    return out
+
+
+def compare(got, ref, dtype, heads=None, label="", bound=None):
+    """Assert parity on all heads or on the listed (b, h) heads.  With
+    `bound` (rounding_bound, all heads), an element also passes when its
+    error lies within that bound."""
     tol = TOL[dtype]
     report = {}
     for name in ("o", "lse", "dq", "dk", "dv"):
@@ -81,6 +120,11 @@ def compare(got, ref, dtype, heads=None, label=""):
             assert err <= tol["lse"], "%s lse: max abs err %.3e > %.1e" % (label, err, tol["lse"])
             continue
         lim = tol["abs"] + tol["rel_elem"] * np.abs(r)
+        if bound is not None:
+            bd = bound[name]
+            if heads is not None:
+                bd = np.stack([bd[b, h] for b, h in heads])
+            lim = np.maximum(lim, bd)
         worst = np.unravel_index(np.argmax(diff - lim), diff.shape)
         assert (diff <= lim).all(), "%s %s: err %.3e at ref %.3e exceeds %.3e" % (
             label, name, diff[worst], r[worst], lim[worst])

@@ -5,7 +5,9 @@ it with its own implementation of the same generator (oracle/philox.py).
 The float32 path is compared at 1e-5, where a single wrong keep bit would
 show (a weight of ~1/T moves the output by ~|v|/T).  The bf16 cases use
 iid N(0, 1) inputs and short rows so that a wrong bit is well above the
-bf16 tolerance too.
+bf16 tolerance too; an element also passes within the first-order bound of
+the bf16 storage roundings (gpu_helpers.rounding_bound), which on these
+short rows stays below the fixed 2e-2 and so does not hide a wrong bit.
 """
 
 import numpy as np
@@ -15,7 +17,7 @@ import torch
 import causal_self_attention_gptattn_amd as G
 from causal_self_attention_gptattn_amd import workloads as W
 
-from gpu_helpers import compare, need_gpu, run_oracle, sample_heads, say, to64
+from gpu_helpers import compare, need_gpu, rounding_bound, run_oracle, sample_heads, say, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -80,7 +82,8 @@ def test_dropout_bf16(B, H, Tq, Tk, off, win, p, D):
     seed, stream = 987654321 + D, 11
     compare(run_drop(inp, dev, off, win, p, seed, stream),
             oracle_drop(inp, off, win, p, seed, stream), "bf16",
-            label="dropout bf16 Tq=%d Tk=%d p=%.2f D=%d" % (Tq, Tk, p, D))
+            label="dropout bf16 Tq=%d Tk=%d p=%.2f D=%d" % (Tq, Tk, p, D),
+            bound=rounding_bound(inp, off, win, p, seed, stream))
 
 
 def test_dropout_full_size_gpt2():
@@ -118,4 +121,5 @@ def test_dropout_autograd_packed():
     gq, gk, gv = G.split_qkv(x.grad, H)
     ref = oracle_drop(inp, 0, 0, 0.3, 99, 2)
     got = {"o": to64(o), "lse": ref["lse"], "dq": to64(gq), "dk": to64(gk), "dv": to64(gv)}
-    compare(got, ref, "bf16", label="dropout autograd packed")
+    compare(got, ref, "bf16", label="dropout autograd packed",
+            bound=rounding_bound(inp, 0, 0, 0.3, 99, 2))
