@@ -94,6 +94,43 @@ def measured_traffic(kernel):
     return int(k["fetch_bytes"] + k["write_bytes"])
 
 
+def cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), else the machine type."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
+def clocks_under_load(run_some_steps):
+    """sclk and power as rocm-smi reports them while steps keep the GPU busy
+    (best effort: None when the tool is missing or fails)."""
+    import subprocess
+
+    try:
+        proc = subprocess.Popen(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t0 = time.time()
+    while proc.poll() is None and time.time() - t0 < 15:
+        run_some_steps()
+    try:
+        out, _ = proc.communicate(timeout=5)
+        rec = json.loads(out)
+    except Exception:  # noqa: BLE001 -- a diagnostic, never fatal
+        proc.kill()
+        return None
+    card = next(iter(rec.values()), {}) if isinstance(rec, dict) else {}
+    keep = {k_: v_ for k_, v_ in card.items()
+            if "sclk" in k_.lower() or "mclk" in k_.lower() or "power" in k_.lower()}
+    return keep or None
+
+
 def cpu_baseline(inp, budget_s):
     """Time the float64 oracle on a bounded sample of whole heads."""
     import numpy as np
@@ -125,7 +162,7 @@ def cpu_baseline(inp, budget_s):
         "kind": "oracle",
         "sample": "%d head-problems (cycling over the %d heads of B=%d, H=%d, T=%d, D=%d), "
                   "float64 numpy oracle forward + backward, %.1f s, %s"
-                  % (done, B * H, B, H, T, D, dt, platform.processor() or platform.machine()),
+                  % (done, B * H, B, H, T, D, dt, cpu_model()),
     }
 
 
@@ -394,6 +431,14 @@ def main():
         }
     traffic = measured_traffic(dom)
 
+    # clocks and power while the step runs (outside every timed region)
+    def some_steps():
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize(dev)
+
+    gpu_state = clocks_under_load(some_steps)
+
     var = None
     if args.variant_steps > 0:
         print("bench: strided entry points", file=sys.stderr, flush=True)
@@ -439,6 +484,7 @@ def main():
             "traffic": traffic,
         },
         "cpu_baseline": base,
+        "gpu_under_load": gpu_state,
         "variants": var,
     }
     print(json.dumps(out), flush=True)
