@@ -90,7 +90,9 @@ __device__ __forceinline__ bf16x8 ld_frag16(const uint16_t* p) {
 // row-major tile X[k][m], lane (c, g) needs k = kb + 4g + {0..3} and
 // kb + 8 + 4g + {0..3} at m = mb + c (the row pattern of a result tile's
 // registers 0..7).  tr_rowoff/tr_coloff give this lane's row and column
-// inside such a 16 x 32 block; ld_frag_tr reads both halves.
+// inside such a 16 x 32 block; ld_frag_tr2 reads its two 8-row halves
+// (rows r and r + 8), each from its own address, as the swizzled LDS
+// layout places them.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int tr_rowoff(int lane) { return 4 * (lane >> 5) + ((lane & 15) >> 2); }
 __device__ __forceinline__ int tr_coloff(int lane) { return 16 * ((lane >> 4) & 1) + 4 * (lane & 3); }
@@ -98,12 +100,12 @@ __device__ __forceinline__ int tr_coloff(int lane) { return 16 * ((lane >> 4) & 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-// p = &X[kb + tr_rowoff][mb + tr_coloff] in LDS, ld = row stride (elements).
-__device__ __forceinline__ bf16x8 ld_frag_tr(const uint16_t* p, int ld) {
-  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
-  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p + 8 * ld));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, lo);
-  const u32x2 h2 = __builtin_bit_cast(u32x2, hi);
+// lo = &X[kb + tr_rowoff][mb + tr_coloff], hi = the same column 8 rows down.
+__device__ __forceinline__ bf16x8 ld_frag_tr2(const uint16_t* lo, const uint16_t* hi) {
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lo));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(hi));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, a);
+  const u32x2 h2 = __builtin_bit_cast(u32x2, b);
   return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
 
@@ -298,16 +300,6 @@ __device__ __forceinline__ int swz_key(int row) {
 template <int D>
 __device__ __forceinline__ int swz(int row, int col) {
   return row * D + (((col >> 3) ^ swz_key<D>(row)) << 3) + (col & 7);
-}
-
-// ld_frag_tr for a swizzled tile: rows r and r + 8 have different keys, so
-// the two halves take their own addresses.
-__device__ __forceinline__ bf16x8 ld_frag_tr2(const uint16_t* lo, const uint16_t* hi) {
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lo));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(hi));
-  const u32x2 l2 = __builtin_bit_cast(u32x2, a);
-  const u32x2 h2 = __builtin_bit_cast(u32x2, b);
-  return __builtin_bit_cast(bf16x8, u32x4{l2[0], l2[1], h2[0], h2[1]});
 }
 
 template <int ROWS, int D, int NT>
