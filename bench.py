@@ -106,7 +106,7 @@ def cpu_model():
     return platform.processor() or platform.machine()
 
 
-def clocks_under_load(run_some_steps):
+def clocks_under_load(run_some_steps, limit_s):
     """sclk and power as rocm-smi reports them while steps keep the GPU busy
     (best effort: None when the tool is missing or fails)."""
     import subprocess
@@ -117,7 +117,7 @@ def clocks_under_load(run_some_steps):
     except OSError:
         return None
     t0 = time.time()
-    while proc.poll() is None and time.time() - t0 < 15:
+    while proc.poll() is None and time.time() - t0 < limit_s:
         run_some_steps()
     try:
         out, _ = proc.communicate(timeout=5)
@@ -283,6 +283,9 @@ def main():
                     help="extra steps timed with the caches flushed before each one")
     ap.add_argument("--variant-steps", type=int, default=20,
                     help="timed steps per strided-entry-point variant (0 = skip them)")
+    ap.add_argument("--smi-seconds", type=float, default=15.0,
+                    help="at most this long, run steps while rocm-smi reads sclk and power "
+                         "(0 = skip)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (calibrates the "
                          "HBM byte counters against a copy of known size) and exit")
@@ -437,7 +440,7 @@ def main():
             step()
         torch.cuda.synchronize(dev)
 
-    gpu_state = clocks_under_load(some_steps)
+    gpu_state = clocks_under_load(some_steps, args.smi_seconds) if args.smi_seconds > 0 else None
 
     var = None
     if args.variant_steps > 0:
