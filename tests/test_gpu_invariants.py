@@ -116,3 +116,27 @@ def test_python_binding_rejects_bad_tensors():
     q16 = torch.zeros(1, 1, 16, 96, dtype=torch.bfloat16, device=dev)
     with pytest.raises(RuntimeError, match="NOT_SUPPORTED"):
         G.fwd(q16, q16.clone(), q16.clone(), 0.1)
+
+
+def test_concurrent_calls_on_two_streams():
+    """The library keeps no state: calls enqueued on two streams at once, on
+    different data, give what each gives alone."""
+    dev = need_gpu()
+    (qa, ka, va, da), sc = gpu_inputs(dev, 2, 4, 600, 64, seed=11)
+    (qb, kb, vb, db), _ = gpu_inputs(dev, 3, 2, 900, 64, seed=12)
+    alone = []
+    for q, k, v, d in ((qa, ka, va, da), (qb, kb, vb, db)):
+        o, lse = G.fwd(q, k, v, sc)
+        alone.append((o, lse) + tuple(G.bwd(q, k, v, o, d, lse, sc)))
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    got = [None, None]
+    for rep in range(3):
+        for i, (s, (q, k, v, d)) in enumerate(zip((s1, s2), ((qa, ka, va, da), (qb, kb, vb, db)))):
+            with torch.cuda.stream(s):
+                o, lse = G.fwd(q, k, v, sc)
+                got[i] = (o, lse) + tuple(G.bwd(q, k, v, o, d, lse, sc))
+        torch.cuda.synchronize()
+        for a, b in zip(alone, got):
+            for x, y in zip(a, b):
+                assert torch.equal(x, y)
