@@ -1,11 +1,12 @@
 """Seeded sweep of the strided entry points against the float64 oracle.
 
-Forty configurations drawn from a fixed seed cover combinations the
-hand-picked cases do not: both precisions and every compiled head size;
-Tq and Tk from 1 to 600 (including Tq > Tk); causal offsets that leave rows
-without keys or let every row see everything; banded windows; dense,
-[B, T, H, D]-transposed and packed [B, T, 3C] layouts; and dropout.  A long
-sequence (16384 positions) is checked on sampled row blocks of the forward
+A hundred and twenty configurations drawn from a fixed seed cover
+combinations the hand-picked cases do not: both precisions and every
+compiled head size; Tq and Tk from 1 to 600 (including Tq > Tk); causal
+offsets that leave rows without keys or let every row see everything;
+banded windows; dense, [B, T, H, D]-transposed and packed [B, T, 3C]
+layouts; and dropout.  A long sequence (16384 positions) is checked on
+sampled row blocks of the forward
 pass, which the oracle computes exactly by shifting the causal offset.
 """
 
@@ -64,7 +65,7 @@ def place(inp, layout, dev, dtype):
     return (qv, kv, vv, do.to(dev)), lambda like: torch.empty_like(like, memory_format=torch.contiguous_format)
 
 
-@pytest.mark.parametrize("cfg", draw_configs(40), ids=lambda c: "c%02d" % c[0])
+@pytest.mark.parametrize("cfg", draw_configs(120), ids=lambda c: "c%03d" % c[0])
 def test_sweep(cfg):
     from oracle import attention as A
     dev = need_gpu()
