@@ -6,8 +6,8 @@ compiled head size; Tq and Tk from 1 to 600 (including Tq > Tk); causal
 offsets that leave rows without keys or let every row see everything;
 banded windows; dense, [B, T, H, D]-transposed and packed [B, T, 3C]
 layouts; and dropout.  A long sequence (16384 positions) is checked on
-sampled row blocks of the forward
-pass, which the oracle computes exactly by shifting the causal offset.
+sampled row blocks of the forward pass, which the oracle computes exactly
+by shifting the causal offset.
 """
 
 import numpy as np
