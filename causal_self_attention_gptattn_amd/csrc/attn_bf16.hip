@@ -124,13 +124,10 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb,
     bf16x8 pf[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      // dropout: keep bits of keys k0 + 32a + 16t + {0..7} + 4g (two groups of four)
+      // dropout: keep bits of keys k0 + 32a + 16t + {0..3, 8..11} + 4g
       uint32_t kb0 = 0, kb1 = 0;
-      if (DROP) {
-        const uint32_t jb = (uint32_t)(k0 + 32 * a + 16 * t) / 4 + g;
-        kb0 = keep_bits(jb, (uint32_t)qi, n, pb);
-        kb1 = keep_bits(jb + 2, (uint32_t)qi, n, pb);
-      }
+      if (DROP)
+        keep_bits_pair((uint32_t)(k0 + 32 * a + 16 * t) / 4 + g, (uint32_t)qi, n, pb, kb0, kb1);
       float p[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -287,11 +284,8 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       uint32_t kb0 = 0, kb1 = 0;
-      if (DROP) {
-        const uint32_t jb = (uint32_t)(k0 + 32 * a + 16 * t) / 4 + g;
-        kb0 = keep_bits(jb, (uint32_t)qi, n, pb);
-        kb1 = keep_bits(jb + 2, (uint32_t)qi, n, pb);
-      }
+      if (DROP)
+        keep_bits_pair((uint32_t)(k0 + 32 * a + 16 * t) / 4 + g, (uint32_t)qi, n, pb, kb0, kb1);
       float ds[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -500,20 +494,24 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
     if (MASK && (h < h0 || h > h1)) continue;  // no query of the block sees these keys
     const f32x16 nl = ld_stats16(ls + 32 * h + 16 * g);
     // Dropout: keep bit of (query 8u + 4g + t of the block, this lane's key)
-    // in bit t of kq[u].  Lane x of each group of four (keys 4 * (kj / 4) + x)
-    // draws the bits of query 8u + 4g + x for all four keys; a transpose
-    // within the group hands each lane its own key's bits.
+    // in bit t of kq[u].  The four lanes of a key group (keys 4 * (kj / 4) +
+    // x) split the draws: lane x draws queries 8x + 4g + {0..3} for all four
+    // keys (two calls, one per query pair), and each lane then takes its own
+    // key's bits from lane u of the group.
     uint32_t kq[4] = {0u, 0u, 0u, 0u};
     f32x16 nd;
     if (DROP) {
       nd = ld_stats16(es + 32 * h + 16 * g);
       const uint32_t x = (uint32_t)(c & 3);
+      const uint32_t ip = (uint32_t)(q0 + 32 * h + 8 * (int)x + 4 * g) >> 1;
+      const uint32_t drawn = keep8((uint32_t)kj >> 2, ip, n, pb) |
+                             keep8((uint32_t)kj >> 2, ip + 1, n, pb) << 8;
+      const uint32_t from[4] = {quad_lane<0>(drawn), quad_lane<1>(drawn), quad_lane<2>(drawn),
+                                quad_lane<3>(drawn)};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const uint32_t mine = keep_bits((uint32_t)kj >> 2,
-                                        (uint32_t)(q0 + 32 * h + 8 * u + 4 * g) + x, n, pb);
-        kq[u] = ((quad_lane<0>(mine) >> x) & 1u) | (((quad_lane<1>(mine) >> x) & 1u) << 1) |
-                (((quad_lane<2>(mine) >> x) & 1u) << 2) | (((quad_lane<3>(mine) >> x) & 1u) << 3);
+        const uint32_t sft = from[u] >> (2 * x);  // bits t = 0, 1 at 0, 1; t = 2, 3 at 8, 9
+        kq[u] = (sft & 3u) | ((sft >> 6) & 12u);
       }
     }
     bf16x8 pf[2], sf[2];
@@ -690,8 +688,8 @@ Problem make_problem(const ProblemArg& p) {
   Problem pb{p.B * p.H, p.H, p.Tq, p.Tk, p.off, p.win, p.scale * kLog2e, p.scale,
              (uint32_t)p.seed, (uint32_t)(p.seed >> 32), p.stream, 0u, 1.0f};
   if (p.dropout > 0.0f) {
-    const double t = ceil((double)p.dropout * 4294967296.0);
-    pb.thr = t >= 4294967295.0 ? 4294967295u : (uint32_t)t;
+    const double t = ceil((double)p.dropout * 65536.0);
+    pb.thr = t >= 65536.0 ? 65536u : (uint32_t)t;
     pb.inv_keep = 1.0f / (1.0f - p.dropout);
   }
   return pb;

@@ -129,12 +129,12 @@ struct Problem {
   // attention dropout (used only by the dropout instantiations)
   uint32_t seed_lo, seed_hi;  // Philox key
   uint32_t stream;            // fourth counter word
-  uint32_t thr;               // drop iff draw < thr, thr = ceil(p * 2^32)
+  uint32_t thr;               // drop iff 16-bit draw < thr, thr = ceil(p * 2^16)
   float inv_keep;             // 1 / (1 - p)
 };
 
 // Kernel-side problem description from the host-side one (launch.h); fills
-// the dropout threshold thr = ceil(p * 2^32) and 1 / (1 - p).
+// the dropout threshold thr = ceil(p * 2^16) and 1 / (1 - p).
 struct ProblemArg;
 Problem make_problem(const ProblemArg& p);
 
@@ -182,9 +182,12 @@ __device__ __forceinline__ int queries_hi(int j1, const Problem& pb) {
 // hi(w0 product) ^ w3 ^ key1, lo(w0 product)); the key advances by
 // 0x9E3779B9 and 0xBB67AE85 between rounds.
 //
-// For head-problem n, query i and key j the draw is word j % 4 of the
-// generator on counter (j / 4, i, n, stream) with key (seed_lo, seed_hi);
-// the weight is kept iff draw >= thr and then scaled by 1 / (1 - p).
+// Each call decides eight weights with 16-bit draws: for head-problem n,
+// query i and key j the generator runs on counter (j / 4, i / 2, n, stream)
+// with key (seed_lo, seed_hi); the draw is the low half of word j % 4 for
+// even i and its high half for odd i.  The weight is kept iff draw >= thr
+// (thr = ceil(p * 2^16), so it is dropped with probability thr / 2^16) and
+// then scaled by 1 / (1 - p).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
                                                uint32_t c3, uint32_t k0, uint32_t k1) {
@@ -204,13 +207,39 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   return u32x4{c0, c1, c2, c3};
 }
 
-// Keep bits of the four keys 4 * jb .. 4 * jb + 3 for query i (bit k = key
-// 4 * jb + k).
-__device__ __forceinline__ uint32_t keep_bits(uint32_t jb, uint32_t i, uint32_t n,
-                                              const Problem& pb) {
-  const u32x4 w = philox4x32_10(jb, i, n, pb.stream, pb.seed_lo, pb.seed_hi);
-  return (w[0] >= pb.thr ? 1u : 0u) | (w[1] >= pb.thr ? 2u : 0u) |
-         (w[2] >= pb.thr ? 4u : 0u) | (w[3] >= pb.thr ? 8u : 0u);
+// Keep bits of one call: keys 4 * jb + m (m = 0..3) for queries 2 * ip and
+// 2 * ip + 1, in bit 2m (even query) and bit 2m + 1 (odd query).
+__device__ __forceinline__ uint32_t keep8(uint32_t jb, uint32_t ip, uint32_t n,
+                                          const Problem& pb) {
+  const u32x4 w = philox4x32_10(jb, ip, n, pb.stream, pb.seed_lo, pb.seed_hi);
+  uint32_t b = 0;
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    b |= ((w[m] & 0xFFFFu) >= pb.thr ? 1u : 0u) << (2 * m) |
+         ((w[m] >> 16) >= pb.thr ? 1u : 0u) << (2 * m + 1);
+  return b;
+}
+
+// Bits 2m + q (m = 0..3) of a keep8 result packed into bits 0..3: the four
+// keys' bits for the query of parity q.
+__device__ __forceinline__ uint32_t keep_of_query(uint32_t b, uint32_t q) {
+  return ((b >> q) & 1u) | ((b >> (1 + q)) & 2u) | ((b >> (2 + q)) & 4u) | ((b >> (3 + q)) & 8u);
+}
+
+// Keep bits of keys 4 * jb .. 4 * jb + 3 (kb0) and 4 * jb + 8 .. 4 * jb + 11
+// (kb1) for query qi, bit k = key k of the group, in kernels where lanes
+// 2x and 2x + 1 hold queries 2y and 2y + 1 with the same jb: the even lane
+// draws group jb and the odd lane group jb + 2, each for both queries, and
+// the two exchange the half the other needs.
+__device__ __forceinline__ void keep_bits_pair(uint32_t jb, uint32_t qi, uint32_t n,
+                                               const Problem& pb, uint32_t& kb0,
+                                               uint32_t& kb1) {
+  const uint32_t odd = qi & 1u;
+  const uint32_t mine = keep8(jb + 2 * odd, qi >> 1, n, pb);
+  // value of lane ^ 1 (DPP quad permute 1, 0, 3, 2)
+  const uint32_t other = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mine, 0xB1, 0xF, 0xF, false);
+  kb0 = keep_of_query(odd ? other : mine, odd);
+  kb1 = keep_of_query(odd ? mine : other, odd);
 }
 
 // Value of v in lane SRC of this lane's group of four (DPP quad permute).

@@ -50,13 +50,14 @@ __device__ __forceinline__ void key_range(int i, const Problem& pb, int& lo, int
 }
 
 // Dropout factor of (query i, key j): 0 or 1 / (1 - p); `bits` caches the
-// keep bits of the four keys of j's group, drawn when j starts a group.
+// keep bits of the call covering j's group of four keys (and query i's
+// pair), drawn when j starts a group.
 template <bool DROP>
 __device__ __forceinline__ float drop_factor(int i, int j, int j0, uint32_t n, uint32_t& bits,
                                              const Problem& pb) {
   if (!DROP) return 1.0f;
-  if (j == j0 || (j & 3) == 0) bits = keep_bits((uint32_t)j >> 2, (uint32_t)i, n, pb);
-  return ((bits >> (j & 3)) & 1u) ? pb.inv_keep : 0.0f;
+  if (j == j0 || (j & 3) == 0) bits = keep8((uint32_t)j >> 2, (uint32_t)i >> 1, n, pb);
+  return ((bits >> (2 * (j & 3) + (i & 1))) & 1u) ? pb.inv_keep : 0.0f;
 }
 
 template <int D, bool DROP>

@@ -196,10 +196,11 @@ size_t gptattn_bwd_workspace_bytes(int B, int H, int T, int D, int is_f32);
  *    normaliser.  The keep mask is not stored: every kernel redraws it from
  *    Philox4x32-10 (Salmon et al., "Parallel Random Numbers: As Easy as 1,
  *    2, 3", SC 2011).  For head-problem n = b*H + h, query i and key j the
- *    draw is word j % 4 of Philox4x32-10 on counter
- *    (j / 4, i, n, rng_stream) with key (seed & 0xffffffff, seed >> 32);
- *    the weight is kept iff draw >= ceil(p * 2^32).  The same problem
- *    (seed, rng_stream, p) must be passed to the forward and backward calls.
+ *    generator runs on counter (j / 4, i / 2, n, rng_stream) with key
+ *    (seed & 0xffffffff, seed >> 32); the draw is the low 16 bits of output
+ *    word j % 4 for even i and its high 16 bits for odd i, and the weight is
+ *    kept iff draw >= ceil(p * 2^16).  The same problem (seed, rng_stream,
+ *    p) must be passed to the forward and backward calls.
  *
  * lse and the workspace stay dense: [B][H][Tq] float32.
  * ------------------------------------------------------------------------ */

@@ -15,11 +15,14 @@ Between rounds the key is bumped by the Weyl constants 0x9E3779B9 and
 over counters.
 
 Dropout mapping (the reading used by the library, see the dropout entry
-points in include/gptattn.h): for head-problem n = b * H + h, query i and
-key j, the generator runs on counter (j // 4, i, n, stream) with key
-(seed & 0xffffffff, seed >> 32); output word j % 4 is the draw x.  The
-weight is kept iff x >= thr, thr = ceil(p * 2^32) (so it is dropped with
-probability thr / 2^32), and a kept weight is scaled by 1 / (1 - p).
+points in include/gptattn.h): the pages fix only the drop probability p, so
+the generator and the width of its draws are this library's choice.  For
+head-problem n = b * H + h, query i and key j, the generator runs on counter
+(j // 4, i // 2, n, stream) with key (seed & 0xffffffff, seed >> 32); the
+draw x is the low 16 bits of output word j % 4 for even i and its high 16
+bits for odd i.  The weight is kept iff x >= thr, thr = ceil(p * 2^16) (so it
+is dropped with probability thr / 2^16), and a kept weight is scaled by
+1 / (1 - p).
 """
 
 import numpy as np
@@ -51,9 +54,10 @@ def philox4x32_10(c0, c1, c2, c3, k0, k1):
 
 
 def threshold(p):
-    """Drop threshold for a float32 dropout probability p in [0, 1)."""
+    """Drop threshold of the 16-bit draws for a float32 dropout probability
+    p in [0, 1)."""
     p = float(np.float32(p))
-    return min(int(np.ceil(p * 2.0 ** 32)), 2 ** 32 - 1) if p > 0 else 0
+    return min(int(np.ceil(p * 2.0 ** 16)), 2 ** 16) if p > 0 else 0
 
 
 def keep_mask(n, Tq, Tk, p, seed, stream=0):
@@ -62,8 +66,9 @@ def keep_mask(n, Tq, Tk, p, seed, stream=0):
         return np.ones((Tq, Tk), dtype=bool)
     i = np.arange(Tq, dtype=np.uint64)[:, None]
     j = np.arange(Tk, dtype=np.uint64)[None, :]
-    words = philox4x32_10(j >> np.uint64(2), i, np.uint64(n), np.uint64(stream),
+    words = philox4x32_10(j >> np.uint64(2), i >> np.uint64(1), np.uint64(n), np.uint64(stream),
                           seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF)
     sel = (j & np.uint64(3)).astype(np.int64)
-    x = np.choose(np.broadcast_to(sel, (Tq, Tk)), [np.broadcast_to(w, (Tq, Tk)) for w in words])
+    w = np.choose(np.broadcast_to(sel, (Tq, Tk)), [np.broadcast_to(w, (Tq, Tk)) for w in words])
+    x = (w >> (np.uint64(16) * (i & np.uint64(1)))) & np.uint64(0xFFFF)
     return x >= np.uint64(threshold(p))

@@ -38,10 +38,12 @@ def test_philox_known_answers(ctr, key, out):
 
 def test_threshold():
     assert P.threshold(0.0) == 0
-    assert P.threshold(0.5) == 2 ** 31
-    assert P.threshold(0.25) == 2 ** 30
+    assert P.threshold(0.5) == 2 ** 15
+    assert P.threshold(0.25) == 2 ** 14
     p = float(np.float32(0.1))
-    assert P.threshold(0.1) == math.ceil(p * 2 ** 32)
+    assert P.threshold(0.1) == math.ceil(p * 2 ** 16)
+    # the largest float32 below 1 drops every weight
+    assert P.threshold(float(np.nextafter(np.float32(1), np.float32(0)))) == 2 ** 16
 
 
 @pytest.mark.parametrize("p", [0.1, 0.5, 0.9])
@@ -64,15 +66,17 @@ def test_masks_differ_across_heads_streams_seeds():
 
 
 def test_mask_word_mapping():
-    """Element (i, j) is word j % 4 of the call on counter (j // 4, i, n, stream)."""
+    """Element (i, j) is the 16-bit half i % 2 (low for even i) of word j % 4
+    of the call on counter (j // 4, i // 2, n, stream)."""
     n, seed, stream, p = 5, 0x123456789ABCDEF, 3, 0.3
     m = P.keep_mask(n, 9, 13, p, seed, stream)
     thr = P.threshold(p)
     for i in range(9):
         for j in range(13):
-            w = P.philox4x32_10(np.uint64(j // 4), np.uint64(i), np.uint64(n), np.uint64(stream),
-                                seed & 0xFFFFFFFF, seed >> 32)
-            assert m[i, j] == (int(w[j % 4]) >= thr)
+            w = P.philox4x32_10(np.uint64(j // 4), np.uint64(i // 2), np.uint64(n),
+                                np.uint64(stream), seed & 0xFFFFFFFF, seed >> 32)
+            x = (int(w[j % 4]) >> (16 * (i % 2))) & 0xFFFF
+            assert m[i, j] == (x >= thr)
 
 
 def rnd(shape, seed):
