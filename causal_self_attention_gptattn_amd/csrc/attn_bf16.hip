@@ -11,8 +11,9 @@
 // longer context) and limited to a band of recent positions (the "locally
 // banded" layers of GPT-3 in the minGPT README notes); see attn_common.h.
 //
-// Kernels (one wave = 64 lanes; every product is v_mfma_f32_32x32x16_bf16,
-// see attn_common.h for the register layout):
+// Kernels (one wave = 64 lanes; the products are v_mfma_f32_32x32x16_bf16,
+// and v_mfma_f32_16x16x32_bf16 in attn_bwd_dkdv16w; see attn_common.h for
+// the register layouts):
 //
 //   attn_fwd      one workgroup = 128 queries of one head (4 waves x 32).
 //                 Walks only the 64-key tiles its rows can see and masks
@@ -34,6 +35,8 @@
 //                 dK^T += Q^T dS with P and dS taken from registers.  Q and dO
 //                 are staged row-major in LDS and read transposed for the
 //                 dV/dK products.
+//   attn_bwd_dkdv16w  the same at D = 128 without dropout, 16 keys per wave on
+//                 the 16 x 16 x 32 product (two waves per SIMD instead of one).
 //
 // The tiles a workgroup walks (K/V, or Q/dO) are copied HBM -> LDS by the
 // gfx950 buffer-load-to-LDS path into two alternating buffers, unpadded and
@@ -54,6 +57,7 @@ constexpr float kLazy = 8.0f;  // log2 headroom before the running max is moved
 constexpr int kBM = 128;       // queries per forward / dQ workgroup
 constexpr int kBN = 64;        // keys per staged K/V tile
 constexpr int kKBN = 128;      // keys per dK/dV workgroup
+constexpr int kKBN16 = 64;     // keys per dK/dV workgroup, 16-key waves (D = 128)
 
 // Key tiles [t0, t1] a query range sees (t1 < t0 when none).
 struct TileSpan {
@@ -671,6 +675,205 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
                 pb.Tk - k0w, lane);
 }
 
+// ---------------------------------------------------------------------------
+// dK/dV at D = 128 without dropout.  With 32 keys per wave the K and V rows
+// (64 registers) and the dK and dV accumulators (128) leave room for one
+// wave per SIMD only.  Here each wave owns 16 keys and uses the 16 x 16 x 32
+// product: K/V rows 32 registers, accumulators 64, two waves per SIMD, and
+// workgroups of 64 keys (twice as many as the 32-key kernel makes).
+// Lane (g, c) owns key c of the wave; S and dP come out with rows = queries
+// 4g + r of each 16-query block, P and dS of two such blocks are packed into
+// one operand, and dV^T / dK^T (rows = head dims 16m + 4g + r, columns =
+// keys) accumulate with dO^T / Q^T read transposed from the swizzled tiles.
+// ---------------------------------------------------------------------------
+
+// One 64-query tile for one wave (16 keys), in two halves of 32 queries.
+template <bool MASK>
+__device__ __forceinline__ void dk16w_tile(const uint16_t* qb, const uint16_t* db, const float* ls,
+                                           const float* es, const bf16x8* kf, const bf16x8* vf,
+                                           f32x4* dvt, f32x4* dkt, int q0, Span seers, int g,
+                                           const int* fo, const int* tlo, int hb0, int hb1,
+                                           const Problem& pb) {
+  constexpr int D = 128, NS = D / 32, NM = D / 16;
+  __builtin_amdgcn_iglp_opt(0);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    // half kk = 16-query blocks 2kk and 2kk + 1; skipped when neither sees a key
+    if (MASK && (2 * kk + 1 < hb0 || 2 * kk > hb1)) continue;
+    // S = Q K^T and dP - delta = dO V^T - delta per block (-delta seeds dP)
+    f32x4 st[2], dp[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = 2 * kk + bb;
+      if (MASK && (b < hb0 || b > hb1)) {
+        st[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[bb] = st[bb];
+        continue;
+      }
+      const f32x4 nd = *reinterpret_cast<const f32x4*>(es + 16 * b + 4 * g);
+      st[bb] = mfma16x16x32(ld_frag16(qb + 16 * b * D + fo[0]), kf[0], f32x4{0.f, 0.f, 0.f, 0.f});
+      dp[bb] = mfma16x16x32(ld_frag16(db + 16 * b * D + fo[0]), vf[0], nd);
+#pragma unroll
+      for (int s = 1; s < NS; ++s) {
+        st[bb] = mfma16x16x32(ld_frag16(qb + 16 * b * D + fo[s]), kf[s], st[bb]);
+        dp[bb] = mfma16x16x32(ld_frag16(db + 16 * b * D + fo[s]), vf[s], dp[bb]);
+      }
+    }
+    float p[8], dsv[8];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = 2 * kk + bb;
+      const f32x4 nl = *reinterpret_cast<const f32x4*>(ls + 16 * b + 4 * g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[bb][r], pb.sl2, nl[r]));
+        if (MASK && !inside(q0 + 16 * b + 4 * g + r, seers)) pv = 0.0f;
+        p[4 * bb + r] = pv;
+        dsv[4 * bb + r] = pv * dp[bb][r];
+      }
+    }
+    // P and dS of the half's 32 queries as one operand each: dV^T += dO^T P
+    // and dK^T += Q^T dS over head-dim blocks m, the transposed reads taking
+    // rows 4g + c / 4 of both blocks (the same query order as the operand)
+    const bf16x8 pf = pack_bf16x8(p), sf = pack_bf16x8(dsv);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int lo = 32 * kk * D + tlo[m], hi = lo + 16 * D;
+      dvt[m] = mfma16x16x32(ld_frag_tr2(db + lo, db + hi), pf, dvt[m]);
+      dkt[m] = mfma16x16x32(ld_frag_tr2(qb + lo, qb + hi), sf, dkt[m]);
+    }
+  }
+}
+
+// Workgroup = 64 keys of one head (4 waves x 16); walks the 64-query tiles
+// that see its keys like attn_bwd_dkdv, with the same double-buffered copies.
+__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv16w(
+    View Q, View K, View V, View dO, const float* __restrict__ LSE,
+    const float* __restrict__ Delta, View dK, View dV, Problem pb) {
+  constexpr int D = 128, BM = 64, BN = kKBN16, NS = D / 32, NM = D / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t QD0[2][BM * D];
+  __shared__ __attribute__((aligned(16))) uint16_t QD1[2][BM * D];
+  __shared__ __attribute__((aligned(16))) float Ls[2][BM];
+  __shared__ __attribute__((aligned(16))) float Es[2][BM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int bid = blockIdx.x;
+  const int kb = bid / pb.N;
+  const int n = bid % pb.N;
+  const uint16_t* Qh = head_of(Q, n, pb.H);
+  const uint16_t* Dh = head_of(dO, n, pb.H);
+  const long long rows = (long long)n * pb.Tq;
+  const int k0 = kb * BN;
+  const int k0w = k0 + 16 * w;
+  const int kj = k0w + c;
+
+  int fo[NS], tlo[NM];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) fo[s] = swz<D>(c, 32 * s + 8 * g);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) tlo[m] = swz<D>(4 * g + (c >> 2), 16 * m + 4 * (c & 3));
+
+  bf16x8 kf[NS], vf[NS];
+  {
+    RowBlock kr, vr;
+    kr.init(head_of(K, n, pb.H) + (long long)k0w * K.st, pb.Tk - k0w, K.st, c);
+    vr.init(head_of(V, n, pb.H) + (long long)k0w * V.st, pb.Tk - k0w, V.st, c);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      kf[s] = __builtin_bit_cast(bf16x8, kr.load(32 * s + 8 * g));
+      vf[s] = __builtin_bit_cast(bf16x8, vr.load(32 * s + 8 * g));
+    }
+  }
+
+  const int qlo = queries_lo(k0, pb), qhi = queries_hi(min(k0 + BN, pb.Tk) - 1, pb);
+  const int qt0 = qlo / BM, qt1 = qhi >= qlo ? qhi / BM : qt0 - 1;
+  const int wqlo = queries_lo(k0w, pb);
+  const int wqhi = k0w < pb.Tk ? queries_hi(min(k0w + 15, pb.Tk - 1), pb) : -1;
+  const Span seers = queries_of(kj, pb);
+
+  TileDMA<BM, D, kThreads> qs, ds;
+  qs.init(tid, Q.st);
+  ds.init(tid, dO.st);
+  float lraw = 0.0f, draw = 0.0f;
+  int qrow = 0;
+  auto load_tile = [&](int qt, int valid, uint16_t (&qd)[2][BM * D]) {
+    const int q1 = qt * BM;
+    qs.load(Qh + (long long)q1 * Q.st, valid, qd[0]);
+    ds.load(Dh + (long long)q1 * dO.st, valid, qd[1]);
+    qrow = q1 + tid;
+    const int cnt = valid < BM ? valid : BM;
+    lraw = load_f32_or_zero(LSE + rows + q1, cnt, tid);
+    draw = load_f32_or_zero(Delta + rows + q1, cnt, tid);
+  };
+  auto publish_tile = [&](int b) {
+    if (tid < BM) {
+      const bool live = qrow < pb.Tq && lraw > -INFINITY;
+      Ls[b][tid] = live ? -lraw * kLog2e : -INFINITY;
+      Es[b][tid] = -draw;
+    }
+    wait_dma();
+  };
+  load_tile(qt0, qt1 >= qt0 ? pb.Tq - qt0 * BM : 0, QD0);
+  publish_tile(0);
+  __syncthreads();
+
+  f32x4 dvt[NM], dkt[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    dvt[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dkt[m] = dvt[m];
+  }
+
+  auto step = [&](int qt, uint16_t (&cur)[2][BM * D], uint16_t (&nxt)[2][BM * D], int b) {
+    const bool more = qt < qt1;
+    if (more) load_tile(qt + 1, pb.Tq - (qt + 1) * BM, nxt);
+    const int q0 = qt * BM;
+    if (q0 + BM - 1 >= wqlo && q0 <= wqhi) {
+      if (needs_mask(q0, q0 + BM - 1, k0w, k0w + 15, pb)) {
+        const int hb0 = max(0, (wqlo - q0) >> 4), hb1 = min(BM / 16 - 1, (wqhi - q0) >> 4);
+        dk16w_tile<true>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers, g, fo, tlo,
+                         hb0, hb1, pb);
+      } else {
+        dk16w_tile<false>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers, g, fo, tlo,
+                          0, BM / 16 - 1, pb);
+      }
+    }
+    if (more) publish_tile(b ^ 1);
+    __syncthreads();
+  };
+  for (int qt = qt0; qt <= qt1; qt += 2) {
+    step(qt, QD0, QD1, 0);
+    if (qt + 1 <= qt1) step(qt + 1, QD1, QD0, 1);
+  }
+
+  // epilogue: lane (g, c) holds key c's dims 16m + 4g + r; 16 rows per wave
+  // staged in LDS (row stride D + 8), then whole rows stored
+  constexpr int LD = D + 8;
+  static_assert(4 * 16 * LD <= 2 * BM * D, "epilogue staging must fit one buffer");
+  uint16_t* stage = &QD0[0][0] + w * 16 * LD;
+  auto store = [&](const f32x4* acc, float mul, View out) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const u32x2 pk = {pack_bf16x2(acc[m][0] * mul, acc[m][1] * mul),
+                        pack_bf16x2(acc[m][2] * mul, acc[m][3] * mul)};
+      *reinterpret_cast<u32x2*>(stage + c * LD + 16 * m + 4 * g) = pk;
+    }
+    __syncthreads();
+    uint16_t* orow = const_cast<uint16_t*>(head_of(out, n, pb.H)) + (long long)k0w * out.st;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int ch = lane + 64 * p, r = ch >> 4, cc = ch & 15;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * LD + 8 * cc);
+      if (r < pb.Tk - k0w) *reinterpret_cast<u32x4*>(orow + (long long)r * out.st + 8 * cc) = v;
+    }
+    __syncthreads();
+  };
+  store(dkt, pb.scale, dK);
+  store(dvt, 1.0f, dV);
+}
+
 template <typename... Args>
 hipError_t launch(void (*kern)(Args...), long long blocks, hipStream_t stream, Args... args) {
   void* argv[] = {static_cast<void*>(&args)...};
@@ -744,7 +947,10 @@ hipError_t launch_bwd_dkdv_bf16(const TensorArg& q, const TensorArg& k, const Te
          lse, delta, view(dk), view(dv), pb)
   switch (p.D) {
     case 64: return drop ? GPTATTN_DKDV(64, 32, true) : GPTATTN_DKDV(64, 64, false);
-    case 128: return drop ? GPTATTN_DKDV(128, 32, true) : GPTATTN_DKDV(128, 32, false);
+    case 128:
+      if (drop) return GPTATTN_DKDV(128, 32, true);
+      return launch(attn_bwd_dkdv16w, (long long)pb.N * ((p.Tk + kKBN16 - 1) / kKBN16), stream,
+                    view(q), view(k), view(v), view(dO), lse, delta, view(dk), view(dv), pb);
     default: return hipErrorInvalidValue;
   }
 #undef GPTATTN_DKDV

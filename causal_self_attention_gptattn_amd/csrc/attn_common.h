@@ -36,6 +36,13 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 16 x 16 result, K = 32, lane l = 16g + c (g = 0..3): the A operand holds
+// A[c][8g + j], the B operand B[8g + j][c], the result D[4g + r][c]
+// (r = 0..3), j = 0..7.  (Measured on the GPU with an in-bounds probe.)
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
