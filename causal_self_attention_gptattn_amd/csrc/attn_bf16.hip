@@ -695,7 +695,7 @@ __device__ __forceinline__ void dk16w_tile(const uint16_t* qb, const uint16_t* d
                                            const int* fo, const int* tlo, int hb0, int hb1,
                                            const Problem& pb) {
   constexpr int D = 128, NS = D / 32, NM = D / 16;
-  __builtin_amdgcn_iglp_opt(0);
+  // (no scheduling hint here: without it this kernel is 2-3% faster)
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     // half kk = 16-query blocks 2kk and 2kk + 1; skipped when neither sees a key
