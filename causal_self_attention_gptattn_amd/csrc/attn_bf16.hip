@@ -29,14 +29,17 @@
 //                 delta_i = sum_d dO_id O_id (written to the workspace for
 //                 attn_bwd_dkdv), then recomputes P^T from lse, dP^T = V dO^T,
 //                 dS^T = P^T (dP^T - delta) and dQ^T += K^T dS^T.
-//   attn_bwd_dkdv one workgroup = 128 keys of one head (4 waves x 32).  Walks
-//                 the query tiles that see its keys with the lane -> key
-//                 layout: S = Q K^T and dP = dO V^T, then dV^T += dO^T P and
+//   attn_bwd_dkdv D = 64 without dropout.  One workgroup = 128 keys of one
+//                 head (4 waves x 32).  Walks the query tiles that see its
+//                 keys with the lane -> key layout: S = Q K^T and
+//                 dP = dO V^T, then dV^T += dO^T P and
 //                 dK^T += Q^T dS with P and dS taken from registers.  Q and dO
 //                 are staged row-major in LDS and read transposed for the
 //                 dV/dK products.
-//   attn_bwd_dkdv16w  the same at D = 128 without dropout, 16 keys per wave on
-//                 the 16 x 16 x 32 product (two waves per SIMD instead of one).
+//   attn_bwd_dkdv16w  the same for D = 128 and for dropout: 16 keys per wave
+//                 on the 16 x 16 x 32 product, which fits two waves per SIMD
+//                 at D = 128 (one with 32 keys) and three at D = 64 with
+//                 dropout.
 //
 // The tiles a workgroup walks (K/V, or Q/dO) are copied HBM -> LDS by the
 // gfx950 buffer-load-to-LDS path into two alternating buffers, unpadded and
@@ -465,17 +468,15 @@ __device__ __forceinline__ f32x16 ld_stats16(const float* p) {
 // hold -lse * log2(e) (-inf for rows that see no key or lie past Tq) and
 // -delta of the tile's queries, permuted by stat_slot; -delta seeds the dP
 // accumulator so that the product yields dP - delta directly.
-template <int D, int BM, bool MASK, bool DROP>
+template <int D, int BM, bool MASK>
 __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db, const float* ls,
                                           const float* es, const bf16x8* kf, const bf16x8* vf,
                                           f32x16* dvt, f32x16* dkt, int q0, Span seers, int g,
-                                          int c, const SwzLane<D>& sw, int kj, uint32_t n, int h0,
-                                          int h1, const Problem& pb) {
+                                          const SwzLane<D>& sw, int h0, int h1, const Problem& pb) {
   // Q and dO tiles: unpadded rows of D, 16-byte chunks swizzled (swz)
   constexpr int DS = D / 16, DE = D / 32, NH = BM / 32;
-  // the same scheduling hint as the forward; with dropout (more registers
-  // live) it makes the compiler spill, so it is left out there
-  if constexpr (!DROP) __builtin_amdgcn_iglp_opt(0);
+  // the same scheduling hint as the forward (2-3% measured)
+  __builtin_amdgcn_iglp_opt(0);
   // All score products of the tile first, so that the matrix cores work on
   // block h + 1 while the vector units turn block h into P and dS.
   f32x16 st[NH], dp[NH];
@@ -483,8 +484,7 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
   for (int h = 0; h < NH; ++h) {
     if (MASK && (h < h0 || h > h1)) continue;  // no query of the block sees these keys
     // S = Q K^T and dP - delta = dO V^T - delta: rows = queries, columns = keys
-    // (with dropout dP starts at 0: delta is subtracted after the mask)
-    const f32x16 nd = DROP ? zero16() : ld_stats16(es + 32 * h + 16 * g);
+    const f32x16 nd = ld_stats16(es + 32 * h + 16 * g);
     st[h] = mfma32x32x16(ld_frag16(qb + 32 * h * D + sw.fo[0]), kf[0], zero16());
     dp[h] = mfma32x32x16(ld_frag16(db + 32 * h * D + sw.fo[0]), vf[0], nd);
 #pragma unroll
@@ -497,27 +497,6 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
   for (int h = 0; h < NH; ++h) {
     if (MASK && (h < h0 || h > h1)) continue;  // no query of the block sees these keys
     const f32x16 nl = ld_stats16(ls + 32 * h + 16 * g);
-    // Dropout: keep bit of (query 8u + 4g + t of the block, this lane's key)
-    // in bit t of kq[u].  The four lanes of a key group (keys 4 * (kj / 4) +
-    // x) split the draws: lane x draws queries 8x + 4g + {0..3} for all four
-    // keys (two calls, one per query pair), and each lane then takes its own
-    // key's bits from lane u of the group.
-    uint32_t kq[4] = {0u, 0u, 0u, 0u};
-    f32x16 nd;
-    if (DROP) {
-      nd = ld_stats16(es + 32 * h + 16 * g);
-      const uint32_t x = (uint32_t)(c & 3);
-      const uint32_t ip = (uint32_t)(q0 + 32 * h + 8 * (int)x + 4 * g) >> 1;
-      const uint32_t drawn = keep8((uint32_t)kj >> 2, ip, n, pb) |
-                             keep8((uint32_t)kj >> 2, ip + 1, n, pb) << 8;
-      const uint32_t from[4] = {quad_lane<0>(drawn), quad_lane<1>(drawn), quad_lane<2>(drawn),
-                                quad_lane<3>(drawn)};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t sft = from[u] >> (2 * x);  // bits t = 0, 1 at 0, 1; t = 2, 3 at 8, 9
-        kq[u] = (sft & 3u) | ((sft >> 6) & 12u);
-      }
-    }
     bf16x8 pf[2], sf[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -527,14 +506,8 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
         const int r = 8 * t + j;
         float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[h][r], pb.sl2, nl[r]));
         if (MASK && !inside(q0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3), seers)) pv = 0.0f;
-        if (DROP) {
-          const bool keep = (kq[r >> 2] >> (r & 3)) & 1u;
-          p[j] = keep ? pv * pb.inv_keep : 0.0f;                        // for dV
-          dsv[j] = pv * ((keep ? dp[h][r] * pb.inv_keep : 0.0f) + nd[r]);  // nd = -delta
-        } else {
-          p[j] = pv;
-          dsv[j] = pv * dp[h][r];
-        }
+        p[j] = pv;
+        dsv[j] = pv * dp[h][r];
       }
       pf[t] = pack_bf16x8(p);
       sf[t] = pack_bf16x8(dsv);
@@ -552,7 +525,7 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db
   }
 }
 
-template <int D, int BM, bool DROP>
+template <int D, int BM>
 __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
     View Q, View K, View V, View dO, const float* __restrict__ LSE,
     const float* __restrict__ Delta, View dK, View dV, Problem pb) {
@@ -648,11 +621,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
       if (needs_mask(q0, q0 + BM - 1, k0w, k0w + 31, pb)) {
         // 32-query blocks of the tile that no key of this wave is seen by
         const int h0 = max(0, (wqlo - q0) >> 5), h1 = min(BM / 32 - 1, (wqhi - q0) >> 5);
-        dkdv_tile<D, BM, true, DROP>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers,
-                                     g, c, sw, kj, n, h0, h1, pb);
+        dkdv_tile<D, BM, true>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers, g, sw,
+                               h0, h1, pb);
       } else {
-        dkdv_tile<D, BM, false, DROP>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers,
-                                      g, c, sw, kj, n, 0, BM / 32 - 1, pb);
+        dkdv_tile<D, BM, false>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers, g, sw,
+                                0, BM / 32 - 1, pb);
       }
     }
     if (more) publish_tile(b ^ 1);
@@ -676,10 +649,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
 }
 
 // ---------------------------------------------------------------------------
-// dK/dV at D = 128 without dropout.  With 32 keys per wave the K and V rows
-// (64 registers) and the dK and dV accumulators (128) leave room for one
-// wave per SIMD only.  Here each wave owns 16 keys and uses the 16 x 16 x 32
-// product: K/V rows 32 registers, accumulators 64, two waves per SIMD, and
+// dK/dV with 16 keys per wave on the 16 x 16 x 32 product: D = 128 (without
+// and with dropout) and D = 64 with dropout.  With 32 keys per wave the
+// D = 128 kernel's K and V rows (64 registers) and dK and dV accumulators
+// (128) leave room for one wave per SIMD; here they take 32 and 64, which
+// gives two waves per SIMD at D = 128 and three at D = 64 with dropout, in
 // workgroups of 64 keys (twice as many as the 32-key kernel makes).
 // Lane (g, c) owns key c of the wave; S and dP come out with rows = queries
 // 4g + r of each 16-query block, P and dS of two such blocks are packed into
@@ -688,19 +662,21 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
 // ---------------------------------------------------------------------------
 
 // One 64-query tile for one wave (16 keys), in two halves of 32 queries.
-template <bool MASK>
+// With dropout, bit 4b + r of kq keeps (query q0 + 16b + 4g + r, this key).
+template <int D, bool MASK, bool DROP>
 __device__ __forceinline__ void dk16w_tile(const uint16_t* qb, const uint16_t* db, const float* ls,
                                            const float* es, const bf16x8* kf, const bf16x8* vf,
                                            f32x4* dvt, f32x4* dkt, int q0, Span seers, int g,
                                            const int* fo, const int* tlo, int hb0, int hb1,
-                                           const Problem& pb) {
-  constexpr int D = 128, NS = D / 32, NM = D / 16;
+                                           uint32_t kq, const Problem& pb) {
+  constexpr int NS = D / 32, NM = D / 16;
   // (no scheduling hint here: without it this kernel is 2-3% faster)
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
     // half kk = 16-query blocks 2kk and 2kk + 1; skipped when neither sees a key
     if (MASK && (2 * kk + 1 < hb0 || 2 * kk > hb1)) continue;
-    // S = Q K^T and dP - delta = dO V^T - delta per block (-delta seeds dP)
+    // S = Q K^T and dP - delta = dO V^T - delta per block (-delta seeds dP;
+    // with dropout dP starts at 0 and delta is added after the keep mask)
     f32x4 st[2], dp[2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
@@ -710,7 +686,8 @@ __device__ __forceinline__ void dk16w_tile(const uint16_t* qb, const uint16_t* d
         dp[bb] = st[bb];
         continue;
       }
-      const f32x4 nd = *reinterpret_cast<const f32x4*>(es + 16 * b + 4 * g);
+      const f32x4 nd =
+          DROP ? f32x4{0.f, 0.f, 0.f, 0.f} : *reinterpret_cast<const f32x4*>(es + 16 * b + 4 * g);
       st[bb] = mfma16x16x32(ld_frag16(qb + 16 * b * D + fo[0]), kf[0], f32x4{0.f, 0.f, 0.f, 0.f});
       dp[bb] = mfma16x16x32(ld_frag16(db + 16 * b * D + fo[0]), vf[0], nd);
 #pragma unroll
@@ -724,12 +701,20 @@ __device__ __forceinline__ void dk16w_tile(const uint16_t* qb, const uint16_t* d
     for (int bb = 0; bb < 2; ++bb) {
       const int b = 2 * kk + bb;
       const f32x4 nl = *reinterpret_cast<const f32x4*>(ls + 16 * b + 4 * g);
+      f32x4 nd;
+      if (DROP) nd = *reinterpret_cast<const f32x4*>(es + 16 * b + 4 * g);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[bb][r], pb.sl2, nl[r]));
         if (MASK && !inside(q0 + 16 * b + 4 * g + r, seers)) pv = 0.0f;
-        p[4 * bb + r] = pv;
-        dsv[4 * bb + r] = pv * dp[bb][r];
+        if (DROP) {
+          const bool keep = (kq >> (4 * b + r)) & 1u;
+          p[4 * bb + r] = keep ? pv * pb.inv_keep : 0.0f;                        // for dV
+          dsv[4 * bb + r] = pv * ((keep ? dp[bb][r] * pb.inv_keep : 0.0f) + nd[r]);  // nd = -delta
+        } else {
+          p[4 * bb + r] = pv;
+          dsv[4 * bb + r] = pv * dp[bb][r];
+        }
       }
     }
     // P and dS of the half's 32 queries as one operand each: dV^T += dO^T P
@@ -747,10 +732,11 @@ __device__ __forceinline__ void dk16w_tile(const uint16_t* qb, const uint16_t* d
 
 // Workgroup = 64 keys of one head (4 waves x 16); walks the 64-query tiles
 // that see its keys like attn_bwd_dkdv, with the same double-buffered copies.
-__global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv16w(
+template <int D, bool DROP>
+__global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void attn_bwd_dkdv16w(
     View Q, View K, View V, View dO, const float* __restrict__ LSE,
     const float* __restrict__ Delta, View dK, View dV, Problem pb) {
-  constexpr int D = 128, BM = 64, BN = kKBN16, NS = D / 32, NM = D / 16;
+  constexpr int BM = 64, BN = kKBN16, NS = D / 32, NM = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t QD0[2][BM * D];
   __shared__ __attribute__((aligned(16))) uint16_t QD1[2][BM * D];
   __shared__ __attribute__((aligned(16))) float Ls[2][BM];
@@ -831,13 +817,30 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv16w(
     if (more) load_tile(qt + 1, pb.Tq - (qt + 1) * BM, nxt);
     const int q0 = qt * BM;
     if (q0 + BM - 1 >= wqlo && q0 <= wqhi) {
+      // Dropout keep bits of the tile: lane x of each quad of keys draws the
+      // 16-query block x for the quad's four keys (two calls, one per query
+      // pair); each lane then takes its own key's bits from lane b.
+      uint32_t kq = 0;
+      if (DROP) {
+        const uint32_t x = (uint32_t)(c & 3);
+        const uint32_t ip = (uint32_t)(q0 + 16 * (int)x + 4 * g) >> 1;
+        const uint32_t drawn = keep8((uint32_t)kj >> 2, ip, (uint32_t)n, pb) |
+                               keep8((uint32_t)kj >> 2, ip + 1, (uint32_t)n, pb) << 8;
+        const uint32_t from[4] = {quad_lane<0>(drawn), quad_lane<1>(drawn),
+                                  quad_lane<2>(drawn), quad_lane<3>(drawn)};
+#pragma unroll
+        for (int bk = 0; bk < 4; ++bk) {
+          const uint32_t sft = from[bk] >> (2 * x);  // queries 0, 1 at bits 0, 1; 2, 3 at 8, 9
+          kq |= ((sft & 3u) | ((sft >> 6) & 12u)) << (4 * bk);
+        }
+      }
       if (needs_mask(q0, q0 + BM - 1, k0w, k0w + 15, pb)) {
         const int hb0 = max(0, (wqlo - q0) >> 4), hb1 = min(BM / 16 - 1, (wqhi - q0) >> 4);
-        dk16w_tile<true>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers, g, fo, tlo,
-                         hb0, hb1, pb);
+        dk16w_tile<D, true, DROP>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers, g,
+                                  fo, tlo, hb0, hb1, kq, pb);
       } else {
-        dk16w_tile<false>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers, g, fo, tlo,
-                          0, BM / 16 - 1, pb);
+        dk16w_tile<D, false, DROP>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers, g,
+                                   fo, tlo, 0, BM / 16 - 1, kq, pb);
       }
     }
     if (more) publish_tile(b ^ 1);
@@ -862,9 +865,10 @@ __global__ __launch_bounds__(kThreads, 2) void attn_bwd_dkdv16w(
     }
     __syncthreads();
     uint16_t* orow = const_cast<uint16_t*>(head_of(out, n, pb.H)) + (long long)k0w * out.st;
+    constexpr int CPR = D / 8;  // 16-byte chunks per row
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int ch = lane + 64 * p, r = ch >> 4, cc = ch & 15;
+    for (int p = 0; p < 16 * CPR / 64; ++p) {
+      const int ch = lane + 64 * p, r = ch / CPR, cc = ch % CPR;
       const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * LD + 8 * cc);
       if (r < pb.Tk - k0w) *reinterpret_cast<u32x4*>(orow + (long long)r * out.st + 8 * cc) = v;
     }
@@ -942,17 +946,19 @@ hipError_t launch_bwd_dkdv_bf16(const TensorArg& q, const TensorArg& k, const Te
   const Problem pb = make_problem(p);
   const long long blocks = (long long)pb.N * ((p.Tk + kKBN - 1) / kKBN);
   const bool drop = p.dropout > 0.0f;
-#define GPTATTN_DKDV(D_, BM_, DROP_)                                                            \
-  launch(attn_bwd_dkdv<D_, BM_, DROP_>, blocks, stream, view(q), view(k), view(v), view(dO),    \
+#define GPTATTN_DKDV(D_, BM_)                                                                   \
+  launch(attn_bwd_dkdv<D_, BM_>, blocks, stream, view(q), view(k), view(v), view(dO), lse,      \
+         delta, view(dk), view(dv), pb)
+  const long long blocks16 = (long long)pb.N * ((p.Tk + kKBN16 - 1) / kKBN16);
+#define GPTATTN_DKDV16(D_, DROP_)                                                               \
+  launch(attn_bwd_dkdv16w<D_, DROP_>, blocks16, stream, view(q), view(k), view(v), view(dO),   \
          lse, delta, view(dk), view(dv), pb)
   switch (p.D) {
-    case 64: return drop ? GPTATTN_DKDV(64, 32, true) : GPTATTN_DKDV(64, 64, false);
-    case 128:
-      if (drop) return GPTATTN_DKDV(128, 32, true);
-      return launch(attn_bwd_dkdv16w, (long long)pb.N * ((p.Tk + kKBN16 - 1) / kKBN16), stream,
-                    view(q), view(k), view(v), view(dO), lse, delta, view(dk), view(dv), pb);
+    case 64: return drop ? GPTATTN_DKDV16(64, true) : GPTATTN_DKDV(64, 64);
+    case 128: return drop ? GPTATTN_DKDV16(128, true) : GPTATTN_DKDV16(128, false);
     default: return hipErrorInvalidValue;
   }
+#undef GPTATTN_DKDV16
 #undef GPTATTN_DKDV
 }
 
