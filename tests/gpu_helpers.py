@@ -133,11 +133,12 @@ def compare(got, ref, dtype, heads=None, label="", bound=None):
         worst = np.unravel_index(np.argmax(diff - lim), diff.shape)
         assert (diff <= lim).all(), "%s %s: err %.3e at ref %.3e exceeds %.3e" % (
             label, name, diff[worst], r[worst], lim[worst])
+        # An exactly zero reference (say one visible key per query, where dS
+        # vanishes identically) is judged by the element-wise limit alone,
+        # which holds the storage-rounding bound when one is given.
         if rnorm > 0:
             assert rel <= tol["rel_fro"], "%s %s: rel Frobenius err %.3e > %.1e" % (
                 label, name, rel, tol["rel_fro"])
-        else:
-            assert err <= tol["abs"]
     say(label, " ".join("%s=%.2e/%.2e" % (n, e, r) for n, (e, r) in report.items()))
     return report
 
