@@ -25,10 +25,12 @@
 //                 O^T += V^T P^T straight from registers.  K and V are staged
 //                 row-major in LDS; V^T is read with the gfx950 transpose
 //                 read (attn_common.h).
-//   attn_bwd_dq   same tiling as attn_fwd.  First forms the row term
+//   attn_bwd_dq   D = 128; same tiling as attn_fwd.  First forms the row term
 //                 delta_i = sum_d dO_id O_id (written to the workspace for
 //                 attn_bwd_dkdv), then recomputes P^T from lse, dP^T = V dO^T,
 //                 dS^T = P^T (dP^T - delta) and dQ^T += K^T dS^T.
+//   attn_bwd_dq16 the same at D = 64 with 16 queries per wave on the
+//                 16 x 16 x 32 product (four waves per SIMD instead of three).
 //   attn_bwd_dkdv D = 64 without dropout.  One workgroup = 128 keys of one
 //                 head (4 waves x 32).  Walks the query tiles that see its
 //                 keys with the lane -> key layout: S = Q K^T and
@@ -757,9 +759,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void attn_bwd_dkdv16w(
 
   int fo[NS], tlo[NM];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) fo[s] = swz<D>(c, 32 * s + 8 * g);
+  for (int s = 0; s < NS; ++s) fo[s] = swz<D, true>(c, 32 * s + 8 * g);
 #pragma unroll
-  for (int m = 0; m < NM; ++m) tlo[m] = swz<D>(4 * g + (c >> 2), 16 * m + 4 * (c & 3));
+  for (int m = 0; m < NM; ++m) tlo[m] = swz<D, true>(4 * g + (c >> 2), 16 * m + 4 * (c & 3));
 
   bf16x8 kf[NS], vf[NS];
   {
@@ -779,7 +781,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void attn_bwd_dkdv16w(
   const int wqhi = k0w < pb.Tk ? queries_hi(min(k0w + 15, pb.Tk - 1), pb) : -1;
   const Span seers = queries_of(kj, pb);
 
-  TileDMA<BM, D, kThreads> qs, ds;
+  TileDMA<BM, D, kThreads, true> qs, ds;
   qs.init(tid, Q.st);
   ds.init(tid, dO.st);
   float lraw = 0.0f, draw = 0.0f;
@@ -878,6 +880,217 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void attn_bwd_dkdv16w(
   store(dvt, 1.0f, dV);
 }
 
+// ---------------------------------------------------------------------------
+// dQ at D = 64 with 16 queries per wave on the 16 x 16 x 32 product: 114
+// registers (126 with dropout), four waves per SIMD, workgroups of 64
+// queries.  Lane (g, c) owns query c of the wave; S^T and dP^T come out with
+// rows = keys 4g + r of each 16-key block; dS^T of two blocks is packed into
+// one operand and dQ^T (rows = head dims 16m + 4g + r, columns = queries)
+// accumulates with K^T read transposed from the swizzled K tile.  (At
+// D = 128 every wave reading the whole K and V tile for 16 queries costs
+// more than the occupancy gains; the 32-query kernel serves it.)
+// ---------------------------------------------------------------------------
+constexpr int kBM16 = 64;  // queries per workgroup (4 waves x 16)
+
+// One 64-key tile for one wave (16 queries), in two halves of 32 keys.  With
+// dropout, bit 4b + r of kq keeps (this query, key k0 + 16b + 4g + r).
+template <int D, bool MASK, bool DROP>
+__device__ __forceinline__ void dq16_tile(const uint16_t* kb, const uint16_t* vb, const bf16x8* qf,
+                                          const bf16x8* df, float nd, float nl, f32x4* acc,
+                                          int k0, Span seen, int g, const int* fo,
+                                          const int* tlo, int hb0, int hb1, uint32_t kq,
+                                          const Problem& pb) {
+  constexpr int NS = D / 32, NM = D / 16;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+    if (MASK && (2 * kk + 1 < hb0 || 2 * kk > hb1)) continue;
+    f32x4 st[2], dp[2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = 2 * kk + bb;
+      if (MASK && (b < hb0 || b > hb1)) {
+        st[bb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dp[bb] = st[bb];
+        continue;
+      }
+      st[bb] = mfma16x16x32(ld_frag16(kb + 16 * b * D + fo[0]), qf[0], f32x4{0.f, 0.f, 0.f, 0.f});
+      dp[bb] = mfma16x16x32(ld_frag16(vb + 16 * b * D + fo[0]), df[0], f32x4{nd, nd, nd, nd});
+#pragma unroll
+      for (int s = 1; s < NS; ++s) {
+        st[bb] = mfma16x16x32(ld_frag16(kb + 16 * b * D + fo[s]), qf[s], st[bb]);
+        dp[bb] = mfma16x16x32(ld_frag16(vb + 16 * b * D + fo[s]), df[s], dp[bb]);
+      }
+    }
+    float ds[8];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int b = 2 * kk + bb;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float p = __builtin_amdgcn_exp2f(__builtin_fmaf(st[bb][r], pb.sl2, nl));
+        if (MASK && !inside(k0 + 16 * b + 4 * g + r, seen)) p = 0.0f;
+        if (DROP) {
+          const float delta = -nd;
+          const bool keep = (kq >> (4 * b + r)) & 1u;
+          ds[4 * bb + r] =
+              p * (keep ? __builtin_fmaf(dp[bb][r] + delta, pb.inv_keep, -delta) : -delta);
+        } else {
+          ds[4 * bb + r] = p * dp[bb][r];
+        }
+      }
+    }
+    const bf16x8 sf = pack_bf16x8(ds);
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int lo = 32 * kk * D + tlo[m], hi = lo + 16 * D;
+      acc[m] = mfma16x16x32(ld_frag_tr2(kb + lo, kb + hi), sf, acc[m]);
+    }
+  }
+}
+
+// Workgroup = 64 queries of one head (4 waves x 16): the row term delta,
+// then the key tiles its rows see, as attn_bwd_dq.
+template <int D, bool DROP>
+__global__ __launch_bounds__(kThreads, 4) void attn_bwd_dq16(
+    View Q, View K, View V, View O, View dO, const float* __restrict__ LSE, View dQ,
+    float* __restrict__ Delta, Problem pb, int nqb) {
+  constexpr int BM = kBM16, BN = kBN, NS = D / 32, NM = D / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t K0[BN * D], K1[BN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t V0[BN * D], V1[BN * D];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int c = lane & 15, g = lane >> 4;
+  const int bid = blockIdx.x;
+  const int qb = nqb - 1 - bid / pb.N;
+  const int n = bid % pb.N;
+  const uint16_t* Kh = head_of(K, n, pb.H);
+  const uint16_t* Vh = head_of(V, n, pb.H);
+  const int q0 = qb * BM;
+  const int q0w = q0 + 16 * w;
+  const int qi = q0w + c;
+  const long long row = (long long)n * pb.Tq + qi;
+
+  int fo[NS], tlo[NM];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) fo[s] = swz<D, true>(c, 32 * s + 8 * g);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) tlo[m] = swz<D, true>(4 * g + (c >> 2), 16 * m + 4 * (c & 3));
+
+  const TileSpan ws = key_tiles(q0, q0 + BM - 1, pb, BN);
+  const TileSpan wv = key_tiles(q0w, q0w + 15, pb, BN);
+  const int wlast = min(q0w + 15, pb.Tq - 1);
+  const Span seen = keys_of(qi, pb);
+  const int wklo = keys_lo(q0w, pb), wkhi = keys_hi(wlast, pb);
+
+  TileDMA<BN, D, kThreads, true> ks, vs;
+  ks.init(tid, K.st);
+  vs.init(tid, V.st);
+  auto load_tile = [&](int kt, int valid, uint16_t* kd, uint16_t* vd) {
+    const int k1 = kt * BN;
+    ks.load(Kh + (long long)k1 * K.st, valid, kd);
+    vs.load(Vh + (long long)k1 * V.st, valid, vd);
+  };
+  load_tile(ws.t0, ws.t1 >= ws.t0 ? pb.Tk - ws.t0 * BN : 0, K0, V0);
+
+  const float lse = qi < pb.Tq ? load_f32_or_zero(LSE + (row - c), pb.Tq - q0w, c) : -INFINITY;
+  bf16x8 qf[NS], df[NS];
+  float dpart = 0.0f;
+  {
+    RowBlock qr, dr, orr;
+    qr.init(head_of(Q, n, pb.H) + (long long)q0w * Q.st, pb.Tq - q0w, Q.st, c);
+    dr.init(head_of(dO, n, pb.H) + (long long)q0w * dO.st, pb.Tq - q0w, dO.st, c);
+    orr.init(head_of(O, n, pb.H) + (long long)q0w * O.st, pb.Tq - q0w, O.st, c);
+    u32x4 ou[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qf[s] = __builtin_bit_cast(bf16x8, qr.load(32 * s + 8 * g));
+      df[s] = __builtin_bit_cast(bf16x8, dr.load(32 * s + 8 * g));
+      ou[s] = orr.load(32 * s + 8 * g);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      const u32x4 du = __builtin_bit_cast(u32x4, df[s]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        dpart += bf16_lo(du[j]) * bf16_lo(ou[s][j]) + bf16_hi(du[j]) * bf16_hi(ou[s][j]);
+    }
+  }
+  // the row's four 16-lane groups hold its four quarters of the head dims
+  dpart += __shfl_xor(dpart, 16);
+  const float delta = dpart + __shfl_xor(dpart, 32);
+  const float nl = lse > -INFINITY ? -lse * kLog2e : -INFINITY;
+  if (qi < pb.Tq && g == 0) Delta[row] = delta;
+
+  wait_dma();
+  __syncthreads();
+
+  f32x4 acc[NM];
+#pragma unroll
+  for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto step = [&](int kt, const uint16_t* kc, const uint16_t* vc, uint16_t* kn, uint16_t* vn) {
+    const bool more = kt < ws.t1;
+    if (more) load_tile(kt + 1, pb.Tk - (kt + 1) * BN, kn, vn);
+    if (kt >= wv.t0 && kt <= wv.t1) {
+      const int k0 = kt * BN;
+      uint32_t kq = 0;
+      if (DROP) {
+        // lanes 2y and 2y + 1 hold queries 2y' and 2y' + 1: the even lane
+        // draws key blocks 0 and 2, the odd lane 1 and 3, each for both
+        // queries, and the two exchange the other half
+        const uint32_t odd = (uint32_t)qi & 1u, ip = (uint32_t)qi >> 1;
+        const uint32_t jb = (uint32_t)k0 / 4 + (uint32_t)g;
+        const uint32_t ma = keep8(jb + 4 * odd, ip, (uint32_t)n, pb);
+        const uint32_t mb = keep8(jb + 8 + 4 * odd, ip, (uint32_t)n, pb);
+        // the neighbour's draws (lane ^ 1, DPP quad permute 1, 0, 3, 2)
+        const uint32_t oa = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)ma, 0xB1, 0xF, 0xF,
+                                                                  false);
+        const uint32_t ob = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)mb, 0xB1, 0xF, 0xF,
+                                                                  false);
+        const uint32_t b0 = odd ? oa : ma, b1 = odd ? ma : oa;
+        const uint32_t b2 = odd ? ob : mb, b3 = odd ? mb : ob;
+        kq = keep_of_query(b0, odd) | keep_of_query(b1, odd) << 4 | keep_of_query(b2, odd) << 8 |
+             keep_of_query(b3, odd) << 12;
+      }
+      if (needs_mask(q0w, wlast, k0, k0 + BN - 1, pb)) {
+        const int hb0 = max(0, (wklo - k0) >> 4), hb1 = min(BN / 16 - 1, (wkhi - k0) >> 4);
+        dq16_tile<D, true, DROP>(kc, vc, qf, df, -delta, nl, acc, k0, seen, g, fo, tlo, hb0, hb1,
+                                 kq, pb);
+      } else {
+        dq16_tile<D, false, DROP>(kc, vc, qf, df, -delta, nl, acc, k0, seen, g, fo, tlo, 0,
+                                  BN / 16 - 1, kq, pb);
+      }
+    }
+    if (more) wait_dma();
+    __syncthreads();
+  };
+  for (int kt = ws.t0; kt <= ws.t1; kt += 2) {
+    step(kt, K0, V0, K1, V1);
+    if (kt + 1 <= ws.t1) step(kt + 1, K1, V1, K0, V0);
+  }
+
+  // epilogue: lane (g, c) holds query c's dims 16m + 4g + r; 16 rows per
+  // wave staged in the K tiles (row stride D + 8), then whole rows stored
+  constexpr int LD = D + 8, CPR = D / 8;
+  static_assert(2 * 16 * LD <= BN * D, "two waves' epilogue staging must fit one K tile");
+  uint16_t* stage = (w < 2 ? K0 : K1) + (w & 1) * 16 * LD;
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const u32x2 pk = {pack_bf16x2(acc[m][0] * pb.scale, acc[m][1] * pb.scale),
+                      pack_bf16x2(acc[m][2] * pb.scale, acc[m][3] * pb.scale)};
+    *reinterpret_cast<u32x2*>(stage + c * LD + 16 * m + 4 * g) = pk;
+  }
+  __syncthreads();
+  uint16_t* orow = const_cast<uint16_t*>(head_of(dQ, n, pb.H)) + (long long)q0w * dQ.st;
+#pragma unroll
+  for (int p = 0; p < 16 * CPR / 64; ++p) {
+    const int ch = lane + 64 * p, r = ch / CPR, cc = ch % CPR;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * LD + 8 * cc);
+    if (r < pb.Tq - q0w) *reinterpret_cast<u32x4*>(orow + (long long)r * dQ.st + 8 * cc) = v;
+  }
+}
+
 template <typename... Args>
 hipError_t launch(void (*kern)(Args...), long long blocks, hipStream_t stream, Args... args) {
   void* argv[] = {static_cast<void*>(&args)...};
@@ -931,11 +1144,17 @@ hipError_t launch_bwd_dq_bf16(const TensorArg& q, const TensorArg& k, const Tens
 #define GPTATTN_DQ(D_, DROP_)                                                                   \
   launch(attn_bwd_dq<D_, DROP_>, blocks, stream, view(q), view(k), view(v), view(o), view(dO),  \
          lse, view(dq), delta, pb, nqb)
+  const int nqb16 = (p.Tq + kBM16 - 1) / kBM16;
+  const long long blocks16 = (long long)pb.N * nqb16;
+#define GPTATTN_DQ16(D_, DROP_)                                                                 \
+  launch(attn_bwd_dq16<D_, DROP_>, blocks16, stream, view(q), view(k), view(v), view(o),        \
+         view(dO), lse, view(dq), delta, pb, nqb16)
   switch (p.D) {
-    case 64: return drop ? GPTATTN_DQ(64, true) : GPTATTN_DQ(64, false);
+    case 64: return drop ? GPTATTN_DQ16(64, true) : GPTATTN_DQ16(64, false);
     case 128: return drop ? GPTATTN_DQ(128, true) : GPTATTN_DQ(128, false);
     default: return hipErrorInvalidValue;
   }
+#undef GPTATTN_DQ16
 #undef GPTATTN_DQ
 }
 

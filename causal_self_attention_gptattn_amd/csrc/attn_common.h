@@ -324,21 +324,29 @@ typedef __attribute__((address_space(3))) void lds_void;
 //     lanes at a time): the four 64-byte chunk groups must land in different
 //     quarters of the window, so the key's bits above the chunk-in-group bits
 //     must differ between rows 4i and 4i+2 (D = 64) or among all four (D = 128).
-template <int D>
+// Tiles read by the kernels with 16-row waves (16 x 16 x 32 products, W16)
+// meet a third pattern: ds_read_b64_tr_b16 of two chunks in rows 4i..4i+3,
+// for two consecutive i at a time (32 lanes).  At D = 64 rows 4i and 4i + 4
+// fall in the same half of the window, and the key above gives their chunk
+// pairs the same two slots (2-way conflicts); 2 ((r / 2) mod 4) + (r / 8)
+// mod 2 separates them and keeps the first pattern conflict-free.  At
+// D = 128 the key above already serves all three patterns.
+template <int D, bool W16 = false>
 __device__ __forceinline__ int swz_key(int row) {
   static_assert(D == 64 || D == 128, "swizzle defined for rows of 64 or 128 elements");
+  if (W16 && D == 64) return 2 * ((row >> 1) & 3) + ((row >> 3) & 1);
   return D == 64 ? ((row & 2) << 1) | ((row >> 2) & 3) : ((row & 3) << 2) | ((row >> 2) & 3);
 }
 
 // Element offset of (row, col) in a swizzled row-major tile of row length D
 // (col a multiple of 4 within one 16-byte chunk, or any col for the chunk's
 // first element).
-template <int D>
+template <int D, bool W16 = false>
 __device__ __forceinline__ int swz(int row, int col) {
-  return row * D + (((col >> 3) ^ swz_key<D>(row)) << 3) + (col & 7);
+  return row * D + (((col >> 3) ^ swz_key<D, W16>(row)) << 3) + (col & 7);
 }
 
-template <int ROWS, int D, int NT>
+template <int ROWS, int D, int NT, bool W16 = false>
 struct TileDMA {
   static constexpr int CPR = D / 8;            // 16-byte chunks per row
   static constexpr int PER = ROWS * CPR / NT;  // chunks per thread
@@ -353,7 +361,7 @@ struct TileDMA {
   __device__ __forceinline__ void init(int tid, long long st) {
     const int row = tid / CPR, slot = tid % CPR;
     rowb = (uint32_t)(st * 2);
-    goff = (uint32_t)row * rowb + 16u * (uint32_t)(slot ^ swz_key<D>(row));
+    goff = (uint32_t)row * rowb + 16u * (uint32_t)(slot ^ swz_key<D, W16>(row));
     gstep = (uint32_t)RSTEP * rowb;
     wofs = (tid & ~63) * 8;
   }

@@ -65,3 +65,24 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert out.returncode == 2
     assert "one GPU" in out.stderr
+
+
+def test_traffic_counters_are_keyed_by_launch(tmp_path):
+    """Counter rows map to the launch they belong to, whichever kernel
+    variant served it."""
+    from causal_self_attention_gptattn_amd import traffic
+
+    rows = [("void gptattn::(anonymous namespace)::attn_fwd<64, false>(...)", 10.0),
+            ("void gptattn::(anonymous namespace)::attn_bwd_dq16<64, false>(...)", 20.0),
+            ("void gptattn::(anonymous namespace)::attn_bwd_dq<128, true>(...)", 40.0),
+            ("void gptattn::(anonymous namespace)::attn_bwd_dkdv<64, 64>(...)", 30.0),
+            ("void gptattn::(anonymous namespace)::attn_bwd_dkdv16w<128, false>(...)", 50.0),
+            ("__amd_rocclr_copyBuffer", 7.0)]
+    path = tmp_path / "c.csv"
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Counter_Name,Counter_Value\n")
+        for name, v in rows:
+            f.write('"%s",FETCH_SIZE,%g\n' % (name, v))
+    got = traffic._per_kernel_kib(str(path), "FETCH_SIZE")
+    assert got == {"attn_fwd": 10.0, "attn_bwd_dq": 30.0, "attn_bwd_dkdv": 40.0,
+                   "__amd_rocclr_copyBuffer": 7.0}
