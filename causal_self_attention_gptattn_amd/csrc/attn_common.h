@@ -314,27 +314,31 @@ struct RowBlock {
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) void lds_void;
 
-// The key depends on r mod 16 and is chosen for the two read patterns of
-// the tiles (64 banks of 4 bytes: a 256-byte window):
-//   ds_read_b128 of one chunk in 16 consecutive rows (16 lanes at a time):
-//     the 16 rows must fill the window once.  D = 64 puts two rows in a
-//     window (row parity picks the half), so the key must take 8 values over
-//     r / 2; D = 128 fills a window per row, so it must take 16 values.
-//   ds_read_b64_tr_b16 of four chunks in 4 consecutive rows 4i..4i+3 (32
-//     lanes at a time): the four 64-byte chunk groups must land in different
-//     quarters of the window, so the key's bits above the chunk-in-group bits
-//     must differ between rows 4i and 4i+2 (D = 64) or among all four (D = 128).
-// Tiles read by the kernels with 16-row waves (16 x 16 x 32 products, W16)
-// meet a third pattern: ds_read_b64_tr_b16 of two chunks in rows 4i..4i+3,
-// for two consecutive i at a time (32 lanes).  At D = 64 rows 4i and 4i + 4
-// fall in the same half of the window, and the key above gives their chunk
-// pairs the same two slots (2-way conflicts); 2 ((r / 2) mod 4) + (r / 8)
-// mod 2 separates them and keeps the first pattern conflict-free.  At
-// D = 128 the key above already serves all three patterns.
+// The key depends on r mod 16 and was chosen by measurement: a probe
+// repeating each operand read of the kernels alone over a tile, under the
+// LDS bank-conflict counter, for each candidate key.
+//   ds_read_b64_tr_b16 (transposed operands) behaves as 64 banks of 4 bytes
+//     serving 32 lanes at a time: conflict-free when the 32 lanes' 8-byte
+//     pieces cover the 256-byte window once.  Every prediction of this rule
+//     over 270 keys matched the counter.
+//   ds_read_b128 (fragments: one chunk in 16 consecutive rows per 16-lane
+//     group) follows no rule of that kind that fits the measurements (a key
+//     that spreads each group's 16 rows over the window can still cost 4
+//     conflict cycles per read), so its keys are measured ones.
+// The 32-row kernels read fragments of one chunk in 32 rows and transposed
+// pieces of four chunks in rows 4i..4i+3; the keys below (W16 = false) are
+// conflict-free for both at D = 64.  The kernels with 16-row waves
+// (16 x 16 x 32 products, W16) read fragments of four chunks in 16 rows and
+// transposed pieces of two chunks in rows 4i..4i+3 for two consecutive i.
+// For them the first key costs 4 conflict cycles per fragment read at
+// D = 64, and at D = 128 4 per fragment read and 2 per transposed read.
+// r mod 8 (D = 64) and the D = 128 key with bit 2 of r also flipping bit 1
+// measure conflict-free for both of their reads.
 template <int D, bool W16 = false>
 __device__ __forceinline__ int swz_key(int row) {
   static_assert(D == 64 || D == 128, "swizzle defined for rows of 64 or 128 elements");
-  if (W16 && D == 64) return 2 * ((row >> 1) & 3) + ((row >> 3) & 1);
+  if (W16)
+    return D == 64 ? (row & 7) : ((row & 3) << 2) | (((row >> 2) & 3) ^ ((row >> 1) & 2));
   return D == 64 ? ((row & 2) << 1) | ((row >> 2) & 3) : ((row & 3) << 2) | ((row >> 2) & 3);
 }
 
