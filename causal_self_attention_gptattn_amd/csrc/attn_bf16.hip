@@ -11,9 +11,9 @@
 // longer context) and limited to a band of recent positions (the "locally
 // banded" layers of GPT-3 in the minGPT README notes); see attn_common.h.
 //
-// Kernels (one wave = 64 lanes; the products are v_mfma_f32_32x32x16_bf16,
-// and v_mfma_f32_16x16x32_bf16 in attn_bwd_dkdv16w; see attn_common.h for
-// the register layouts):
+// Kernels (one wave = 64 lanes; the products are v_mfma_f32_32x32x16_bf16
+// in attn_fwd and attn_bwd_dq, v_mfma_f32_16x16x32_bf16 in attn_bwd_dq16 and
+// attn_bwd_dkdv16w; see attn_common.h for the register layouts):
 //
 //   attn_fwd      one workgroup = 128 queries of one head (4 waves x 32).
 //                 Walks only the 64-key tiles its rows can see and masks
@@ -27,21 +27,17 @@
 //                 read (attn_common.h).
 //   attn_bwd_dq   D = 128; same tiling as attn_fwd.  First forms the row term
 //                 delta_i = sum_d dO_id O_id (written to the workspace for
-//                 attn_bwd_dkdv), then recomputes P^T from lse, dP^T = V dO^T,
-//                 dS^T = P^T (dP^T - delta) and dQ^T += K^T dS^T.
+//                 attn_bwd_dkdv16w), then recomputes P^T from lse,
+//                 dP^T = V dO^T, dS^T = P^T (dP^T - delta) and
+//                 dQ^T += K^T dS^T.
 //   attn_bwd_dq16 the same at D = 64 with 16 queries per wave on the
 //                 16 x 16 x 32 product (four waves per SIMD instead of three).
-//   attn_bwd_dkdv D = 64 without dropout.  One workgroup = 128 keys of one
-//                 head (4 waves x 32).  Walks the query tiles that see its
-//                 keys with the lane -> key layout: S = Q K^T and
-//                 dP = dO V^T, then dV^T += dO^T P and
-//                 dK^T += Q^T dS with P and dS taken from registers.  Q and dO
-//                 are staged row-major in LDS and read transposed for the
-//                 dV/dK products.
-//   attn_bwd_dkdv16w  the same for D = 128 and for dropout: 16 keys per wave
-//                 on the 16 x 16 x 32 product, which fits two waves per SIMD
-//                 at D = 128 (one with 32 keys) and three at D = 64 with
-//                 dropout.
+//   attn_bwd_dkdv16w  one workgroup = 64 keys of one head (4 waves x 16).
+//                 Walks the query tiles that see its keys with the
+//                 lane -> key layout: S = Q K^T and dP = dO V^T, then
+//                 dV^T += dO^T P and dK^T += Q^T dS with P and dS taken from
+//                 registers.  Q and dO are staged row-major in LDS and read
+//                 transposed for the dV/dK products.
 //
 // The tiles a workgroup walks (K/V, or Q/dO) are copied HBM -> LDS by the
 // gfx950 buffer-load-to-LDS path into two alternating buffers, unpadded and
@@ -61,8 +57,7 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr float kLazy = 8.0f;  // log2 headroom before the running max is moved
 constexpr int kBM = 128;       // queries per forward / dQ workgroup
 constexpr int kBN = 64;        // keys per staged K/V tile
-constexpr int kKBN = 128;      // keys per dK/dV workgroup
-constexpr int kKBN16 = 64;     // keys per dK/dV workgroup, 16-key waves (D = 128)
+constexpr int kKBN16 = 64;     // keys per dK/dV workgroup (4 waves x 16)
 
 // Key tiles [t0, t1] a query range sees (t1 < t0 when none).
 struct TileSpan {
@@ -442,221 +437,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void attn_bwd_dq(
 }
 
 // ---------------------------------------------------------------------------
-// Backward, part 2: dK and dV (lane -> key layout)
-// ---------------------------------------------------------------------------
-
-// Query-row statistics in LDS are stored permuted so that the 16 rows a
-// lane half needs for one 32-query block (rows 8u + 4g + i in result-
-// register order r = 4u + i) are contiguous: row q of the tile goes to
-// slot 32 (q / 32) + 16 ((q % 8) / 4) + 4 ((q % 32) / 8) + q % 4.
-__device__ __forceinline__ int stat_slot(int q) {
-  return 32 * (q >> 5) + 16 * ((q & 7) >> 2) + 4 * ((q & 31) >> 3) + (q & 3);
-}
-
-// 16 consecutive row statistics from LDS as four 16-byte reads.  A single
-// 64-byte read would be split by the compiler into pieces that no longer
-// carry the information that they do not overlap the Q / dO copies still in
-// flight, and each piece would then wait for those copies.
-__device__ __forceinline__ f32x16 ld_stats16(const float* p) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
-  const f32x4 c = *reinterpret_cast<const f32x4*>(p + 8);
-  const f32x4 d = *reinterpret_cast<const f32x4*>(p + 12);
-  return f32x16{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3],
-                c[0], c[1], c[2], c[3], d[0], d[1], d[2], d[3]};
-}
-
-// One BM-query tile for one wave (32 keys, one per lane column c).  ls/es
-// hold -lse * log2(e) (-inf for rows that see no key or lie past Tq) and
-// -delta of the tile's queries, permuted by stat_slot; -delta seeds the dP
-// accumulator so that the product yields dP - delta directly.
-template <int D, int BM, bool MASK>
-__device__ __forceinline__ void dkdv_tile(const uint16_t* qb, const uint16_t* db, const float* ls,
-                                          const float* es, const bf16x8* kf, const bf16x8* vf,
-                                          f32x16* dvt, f32x16* dkt, int q0, Span seers, int g,
-                                          const SwzLane<D>& sw, int h0, int h1, const Problem& pb) {
-  // Q and dO tiles: unpadded rows of D, 16-byte chunks swizzled (swz)
-  constexpr int DS = D / 16, DE = D / 32, NH = BM / 32;
-  // the same scheduling hint as the forward (2-3% measured)
-  __builtin_amdgcn_iglp_opt(0);
-  // All score products of the tile first, so that the matrix cores work on
-  // block h + 1 while the vector units turn block h into P and dS.
-  f32x16 st[NH], dp[NH];
-#pragma unroll
-  for (int h = 0; h < NH; ++h) {
-    if (MASK && (h < h0 || h > h1)) continue;  // no query of the block sees these keys
-    // S = Q K^T and dP - delta = dO V^T - delta: rows = queries, columns = keys
-    const f32x16 nd = ld_stats16(es + 32 * h + 16 * g);
-    st[h] = mfma32x32x16(ld_frag16(qb + 32 * h * D + sw.fo[0]), kf[0], zero16());
-    dp[h] = mfma32x32x16(ld_frag16(db + 32 * h * D + sw.fo[0]), vf[0], nd);
-#pragma unroll
-    for (int s = 1; s < DS; ++s) {
-      st[h] = mfma32x32x16(ld_frag16(qb + 32 * h * D + sw.fo[s]), kf[s], st[h]);
-      dp[h] = mfma32x32x16(ld_frag16(db + 32 * h * D + sw.fo[s]), vf[s], dp[h]);
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < NH; ++h) {
-    if (MASK && (h < h0 || h > h1)) continue;  // no query of the block sees these keys
-    const f32x16 nl = ld_stats16(ls + 32 * h + 16 * g);
-    bf16x8 pf[2], sf[2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      float p[8], dsv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = 8 * t + j;
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(st[h][r], pb.sl2, nl[r]));
-        if (MASK && !inside(q0 + 32 * h + 8 * (r >> 2) + 4 * g + (r & 3), seers)) pv = 0.0f;
-        p[j] = pv;
-        dsv[j] = pv * dp[h][r];
-      }
-      pf[t] = pack_bf16x8(p);
-      sf[t] = pack_bf16x8(dsv);
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS, dO^T and Q^T read transposed
-#pragma unroll
-    for (int e = 0; e < DE; ++e)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int rb = (32 * h + 16 * t) * D;
-        const int lo = rb + sw.tlo[e], hi = rb + sw.thi[e];
-        dvt[e] = mfma32x32x16(ld_frag_tr2(db + lo, db + hi), pf[t], dvt[e]);
-        dkt[e] = mfma32x32x16(ld_frag_tr2(qb + lo, qb + hi), sf[t], dkt[e]);
-      }
-  }
-}
-
-template <int D, int BM>
-__global__ __launch_bounds__(kThreads, D == 64 ? 2 : 1) void attn_bwd_dkdv(
-    View Q, View K, View V, View dO, const float* __restrict__ LSE,
-    const float* __restrict__ Delta, View dK, View dV, Problem pb) {
-  constexpr int BN = kKBN;
-  constexpr int DS = D / 16;
-  constexpr int DE = D / 32;
-  // Q and dO tiles of the two buffers, copied in by the DMA (unpadded,
-  // swizzled).  Separate arrays per buffer, and a loop unrolled by two, let
-  // the compiler see that the copy into one buffer does not touch the one
-  // being read, so reads do not wait for the copy.
-  __shared__ __attribute__((aligned(16))) uint16_t QD0[2][BM * D];
-  __shared__ __attribute__((aligned(16))) uint16_t QD1[2][BM * D];
-  __shared__ __attribute__((aligned(64))) float Ls[2][BM];
-  __shared__ __attribute__((aligned(64))) float Es[2][BM];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
-  const int c = lane & 31, g = lane >> 5;
-  SwzLane<D> sw;
-  sw.init(c, g, tr_rowoff(lane), tr_coloff(lane));
-  const int bid = blockIdx.x;
-  const int kb = bid / pb.N;  // under plain causal masking, block 0 has the most queries
-  const int n = bid % pb.N;
-  const uint16_t* Qh = head_of(Q, n, pb.H);
-  const uint16_t* Dh = head_of(dO, n, pb.H);
-  const long long rows = (long long)n * pb.Tq;
-  const int k0 = kb * BN;
-  const int k0w = k0 + 32 * w;
-  const int kj = k0w + c;
-
-  bf16x8 kf[DS], vf[DS];  // this lane's key rows of K and V (zero past Tk)
-  {
-    RowBlock kr, vr;
-    kr.init(head_of(K, n, pb.H) + (long long)k0w * K.st, pb.Tk - k0w, K.st, c);
-    vr.init(head_of(V, n, pb.H) + (long long)k0w * V.st, pb.Tk - k0w, V.st, c);
-#pragma unroll
-    for (int s = 0; s < DS; ++s) {
-      kf[s] = __builtin_bit_cast(bf16x8, kr.load(16 * s + 8 * g));
-      vf[s] = __builtin_bit_cast(bf16x8, vr.load(16 * s + 8 * g));
-    }
-  }
-
-  // query tiles that see the workgroup's keys; queries that see this wave's
-  const int qlo = queries_lo(k0, pb), qhi = queries_hi(min(k0 + BN, pb.Tk) - 1, pb);
-  const int qt0 = qlo / BM, qt1 = qhi >= qlo ? qhi / BM : qt0 - 1;
-  const int wqlo = queries_lo(k0w, pb);
-  const int wqhi = k0w < pb.Tk ? queries_hi(min(k0w + 31, pb.Tk - 1), pb) : -1;
-  const Span seers = queries_of(kj, pb);  // queries that see this lane's key
-
-  TileDMA<BM, D, kThreads> qs, ds;
-  qs.init(tid, Q.st);
-  ds.init(tid, dO.st);
-  // Row statistics of the tile: thread t < BM loads query q1 + t.  The loads
-  // only issue here; they are turned into -lse * log2(e) and -delta when the
-  // tile is published, so that the compute in between does not wait for them.
-  float lraw = 0.0f, draw = 0.0f;
-  int qrow = 0;
-  auto load_tile = [&](int qt, int valid, uint16_t (&qd)[2][BM * D]) {
-    const int q1 = qt * BM;
-    qs.load(Qh + (long long)q1 * Q.st, valid, qd[0]);
-    ds.load(Dh + (long long)q1 * dO.st, valid, qd[1]);
-    qrow = q1 + tid;
-    const int cnt = valid < BM ? valid : BM;  // threads tid >= BM read past it: zero
-    lraw = load_f32_or_zero(LSE + rows + q1, cnt, tid);
-    draw = load_f32_or_zero(Delta + rows + q1, cnt, tid);
-  };
-  auto publish_tile = [&](int b) {
-    if (tid < BM) {
-      const bool live = qrow < pb.Tq && lraw > -INFINITY;  // rows past Tq or seeing no key
-      Ls[b][stat_slot(tid)] = live ? -lraw * kLog2e : -INFINITY;
-      Es[b][stat_slot(tid)] = -draw;
-    }
-    wait_dma();  // this wave's tile copies have landed; the barrier publishes them
-  };
-  load_tile(qt0, qt1 >= qt0 ? pb.Tq - qt0 * BM : 0, QD0);
-  publish_tile(0);
-  __syncthreads();
-
-  f32x16 dvt[DE], dkt[DE];
-#pragma unroll
-  for (int e = 0; e < DE; ++e) {
-    dvt[e] = zero16();
-    dkt[e] = zero16();
-  }
-
-  // one tile: compute on buffer `cur` (index b) while the next tile is
-  // copied into buffer `nxt`
-  auto step = [&](int qt, uint16_t (&cur)[2][BM * D], uint16_t (&nxt)[2][BM * D], int b) {
-    const bool more = qt < qt1;
-    if (more) load_tile(qt + 1, pb.Tq - (qt + 1) * BM, nxt);
-    const int q0 = qt * BM;
-    if (q0 + BM - 1 >= wqlo && q0 <= wqhi) {  // some query of the tile sees a key of this wave
-      if (needs_mask(q0, q0 + BM - 1, k0w, k0w + 31, pb)) {
-        // 32-query blocks of the tile that no key of this wave is seen by
-        const int h0 = max(0, (wqlo - q0) >> 5), h1 = min(BM / 32 - 1, (wqhi - q0) >> 5);
-        dkdv_tile<D, BM, true>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers, g, sw,
-                               h0, h1, pb);
-      } else {
-        dkdv_tile<D, BM, false>(cur[0], cur[1], Ls[b], Es[b], kf, vf, dvt, dkt, q0, seers, g, sw,
-                                0, BM / 32 - 1, pb);
-      }
-    }
-    if (more) publish_tile(b ^ 1);
-    __syncthreads();
-  };
-  for (int qt = qt0; qt <= qt1; qt += 2) {
-    step(qt, QD0, QD1, 0);
-    if (qt + 1 <= qt1) step(qt + 1, QD1, QD0, 1);
-  }
-
-  // the Q / dO tiles are free after the loop's last barrier: 16 rows per wave
-  constexpr int LD = D + 8;
-  static_assert(2 * 16 * LD <= 2 * BM * D, "two waves' epilogue staging must fit one buffer");
-  uint16_t* stage = (w < 2 ? &QD0[0][0] : &QD1[0][0]) + (w & 1) * 16 * LD;
-  store_rows<D>(stage, dkt, pb.scale,
-                const_cast<uint16_t*>(head_of(dK, n, pb.H)) + (long long)k0w * dK.st, dK.st,
-                pb.Tk - k0w, lane);
-  store_rows<D>(stage, dvt, 1.0f,
-                const_cast<uint16_t*>(head_of(dV, n, pb.H)) + (long long)k0w * dV.st, dV.st,
-                pb.Tk - k0w, lane);
-}
-
-// ---------------------------------------------------------------------------
-// dK/dV with 16 keys per wave on the 16 x 16 x 32 product: D = 128 (without
-// and with dropout) and D = 64 with dropout.  With 32 keys per wave the
-// D = 128 kernel's K and V rows (64 registers) and dK and dV accumulators
-// (128) leave room for one wave per SIMD; here they take 32 and 64, which
-// gives two waves per SIMD at D = 128 and three at D = 64 with dropout, in
-// workgroups of 64 keys (twice as many as the 32-key kernel makes).
+// Backward, part 2: dK and dV (lane -> key layout), 16 keys per wave on the
+// 16 x 16 x 32 product.  The K and V rows a wave keeps in registers take 32
+// registers and the dK and dV accumulators 64 (with 32 keys per wave, 64 and
+// 128: one wave per SIMD at D = 128, two at D = 64).  Two waves per SIMD at
+// D = 128, three at D = 64, in workgroups of 64 keys.
 // Lane (g, c) owns key c of the wave; S and dP come out with rows = queries
 // 4g + r of each 16-query block, P and dS of two such blocks are packed into
 // one operand, and dV^T / dK^T (rows = head dims 16m + 4g + r, columns =
@@ -733,7 +518,8 @@ __device__ __forceinline__ void dk16w_tile(const uint16_t* qb, const uint16_t* d
 }
 
 // Workgroup = 64 keys of one head (4 waves x 16); walks the 64-query tiles
-// that see its keys like attn_bwd_dkdv, with the same double-buffered copies.
+// that see its keys, from the diagonal to the end, with double-buffered
+// Q / dO copies and the tiles' lse and delta staged beside them.
 template <int D, bool DROP>
 __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void attn_bwd_dkdv16w(
     View Q, View K, View V, View dO, const float* __restrict__ LSE,
@@ -1163,22 +949,17 @@ hipError_t launch_bwd_dkdv_bf16(const TensorArg& q, const TensorArg& k, const Te
                                 const TensorArg& dk, const TensorArg& dv, const ProblemArg& p,
                                 hipStream_t stream) {
   const Problem pb = make_problem(p);
-  const long long blocks = (long long)pb.N * ((p.Tk + kKBN - 1) / kKBN);
   const bool drop = p.dropout > 0.0f;
-#define GPTATTN_DKDV(D_, BM_)                                                                   \
-  launch(attn_bwd_dkdv<D_, BM_>, blocks, stream, view(q), view(k), view(v), view(dO), lse,      \
-         delta, view(dk), view(dv), pb)
-  const long long blocks16 = (long long)pb.N * ((p.Tk + kKBN16 - 1) / kKBN16);
+  const long long blocks = (long long)pb.N * ((p.Tk + kKBN16 - 1) / kKBN16);
 #define GPTATTN_DKDV16(D_, DROP_)                                                               \
-  launch(attn_bwd_dkdv16w<D_, DROP_>, blocks16, stream, view(q), view(k), view(v), view(dO),   \
+  launch(attn_bwd_dkdv16w<D_, DROP_>, blocks, stream, view(q), view(k), view(v), view(dO),     \
          lse, delta, view(dk), view(dv), pb)
   switch (p.D) {
-    case 64: return drop ? GPTATTN_DKDV16(64, true) : GPTATTN_DKDV(64, 64);
+    case 64: return drop ? GPTATTN_DKDV16(64, true) : GPTATTN_DKDV16(64, false);
     case 128: return drop ? GPTATTN_DKDV16(128, true) : GPTATTN_DKDV16(128, false);
     default: return hipErrorInvalidValue;
   }
 #undef GPTATTN_DKDV16
-#undef GPTATTN_DKDV
 }
 
 }  // namespace gptattn
