@@ -68,11 +68,6 @@ __device__ __forceinline__ TileSpan key_tiles(int i0, int i1, const Problem& pb,
   return TileSpan{lo / bn, hi >= lo ? hi / bn : lo / bn - 1};
 }
 
-// Does some query in [i0, i1] fail to see some key in [j0, j1]?  Only such
-// tiles pay for the element-wise mask.
-__device__ __forceinline__ bool needs_mask(int i0, int i1, int j0, int j1, const Problem& pb) {
-  return j1 > i0 + pb.off || j1 >= pb.Tk || (pb.win > 0 && j0 <= i1 + pb.off - pb.win);
-}
 
 // ---------------------------------------------------------------------------
 // Forward
@@ -396,7 +391,12 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void attn_bwd_dq(
   }
   const float delta = half_sum(dpart);
   const float nl = lse > -INFINITY ? -lse * kLog2e : -INFINITY;
-  if (qi < pb.Tq && g == 0) Delta[row] = delta;
+  if (qi < pb.Tq && g == 0) {
+    // workspace: -delta, then the seed -lse/scale of the head-size-64
+    // dK/dV kernel's score accumulator (-inf for a query that sees nothing)
+    Delta[row] = -delta;
+    Delta[(long long)pb.N * pb.Tq + row] = lse > -INFINITY ? -lse / pb.scale : -INFINITY;
+  }
   f32x16 nd;
 #pragma unroll
   for (int r = 0; r < 16; ++r) nd[r] = -delta;
@@ -585,7 +585,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void attn_bwd_dkdv16w(
     if (tid < BM) {
       const bool live = qrow < pb.Tq && lraw > -INFINITY;
       Ls[b][tid] = live ? -lraw * kLog2e : -INFINITY;
-      Es[b][tid] = -draw;
+      Es[b][tid] = draw;  // the workspace holds -delta
     }
     wait_dma();
   };
@@ -806,7 +806,12 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bwd_dq16(
   dpart += __shfl_xor(dpart, 16);
   const float delta = dpart + __shfl_xor(dpart, 32);
   const float nl = lse > -INFINITY ? -lse * kLog2e : -INFINITY;
-  if (qi < pb.Tq && g == 0) Delta[row] = delta;
+  if (qi < pb.Tq && g == 0) {
+    // workspace: -delta, then the seed -lse/scale of the head-size-64
+    // dK/dV kernel's score accumulator (-inf for a query that sees nothing)
+    Delta[row] = -delta;
+    Delta[(long long)pb.N * pb.Tq + row] = lse > -INFINITY ? -lse / pb.scale : -INFINITY;
+  }
 
   wait_dma();
   __syncthreads();
@@ -948,8 +953,9 @@ hipError_t launch_bwd_dkdv_bf16(const TensorArg& q, const TensorArg& k, const Te
                                 const TensorArg& dO, const float* lse, const float* delta,
                                 const TensorArg& dk, const TensorArg& dv, const ProblemArg& p,
                                 hipStream_t stream) {
-  const Problem pb = make_problem(p);
   const bool drop = p.dropout > 0.0f;
+  if (p.D == 64 && !drop) return launch_bwd_dkdv_d64(q, k, v, dO, lse, delta, dk, dv, p, stream);
+  const Problem pb = make_problem(p);
   const long long blocks = (long long)pb.N * ((p.Tk + kKBN16 - 1) / kKBN16);
 #define GPTATTN_DKDV16(D_, DROP_)                                                               \
   launch(attn_bwd_dkdv16w<D_, DROP_>, blocks, stream, view(q), view(k), view(v), view(dO),     \

@@ -173,6 +173,11 @@ __device__ __forceinline__ int keys_lo(int i0, const Problem& pb) {
 __device__ __forceinline__ int keys_hi(int i1, const Problem& pb) {
   return min(pb.Tk - 1, i1 + pb.off);
 }
+// Does some query in [i0, i1] fail to see some key in [j0, j1] (or is some
+// key past the end)?  Only such tiles pay for the element-wise mask.
+__device__ __forceinline__ bool needs_mask(int i0, int i1, int j0, int j1, const Problem& pb) {
+  return j1 > i0 + pb.off || j1 >= pb.Tk || (pb.win > 0 && j0 <= i1 + pb.off - pb.win);
+}
 // First / last query that sees some key in [j0, j1].
 __device__ __forceinline__ int queries_lo(int j0, const Problem& pb) {
   return max(0, j0 - pb.off);
@@ -407,6 +412,13 @@ struct SwzLane {
 
 // Wait for this wave's outstanding global loads, including copies into LDS.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The same wait as a real s_waitcnt instruction (vmcnt(0), the other counters
+// left alone: expcnt 7, lgkmcnt 15), which the compiler's own wait insertion
+// takes into account: registers loaded before it count as arrived, so no
+// wait for them is placed later (inside a loop that follows, every
+// iteration would otherwise wait for that iteration's tile copies).
+__device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // ---------------------------------------------------------------------------
 // Epilogue: a wave's 32 x D block of results, held in the MFMA result layout

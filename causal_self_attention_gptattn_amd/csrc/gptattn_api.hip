@@ -99,15 +99,17 @@ int check_bwd(const Buf* ins, int nin, const Buf* outs, int nout, const void* ws
   if (!sizes(B, H, T, D, elem, &tb, &rb)) return GPTATTN_ERROR_INVALID_VALUE;
   if (!scale_ok(scale)) return GPTATTN_ERROR_INVALID_VALUE;
   if (!head_ok) return GPTATTN_ERROR_NOT_SUPPORTED;
-  if (!ws || !aligned(ws) || ws_bytes < rb) return GPTATTN_ERROR_WORKSPACE;
+  // the workspace holds two [B][H][T] float vectors (see include/gptattn.h)
+  const size_t wb = 2 * rb;
+  if (!ws || !aligned(ws) || ws_bytes < wb) return GPTATTN_ERROR_WORKSPACE;
   Range ri[8], ro[8];
   int ni = 0, no = 0;
   for (int i = 0; i < nin; ++i) ri[ni++] = rng(ins[i].p, ins[i].rows ? rb : tb);
   for (int i = 0; i < nout; ++i) ro[no++] = rng(outs[i].p, outs[i].rows ? rb : tb);
   if (ws_is_output) {
-    ro[no++] = rng(ws, rb);
+    ro[no++] = rng(ws, wb);
   } else {
-    ri[ni++] = rng(ws, rb);
+    ri[ni++] = rng(ws, wb);
   }
   if (!outputs_disjoint(ro, no, ri, ni)) return GPTATTN_ERROR_INVALID_VALUE;
   return GPTATTN_SUCCESS;
@@ -455,9 +457,10 @@ GPTATTN_API int gptattn_bwd_ex(const gptattn_problem* p, const gptattn_tensor* q
                           lattice(*v, B, H, Tk, D, elem), lattice(*o, B, H, Tq, D, elem),
                           lattice(*dO, B, H, Tq, D, elem), contiguous(lse, rb)};
   const Lattice outs[4] = {lattice(*dq, B, H, Tq, D, elem), lattice(*dk, B, H, Tk, D, elem),
-                           lattice(*dv, B, H, Tk, D, elem), contiguous(workspace, rb)};
+                           lattice(*dv, B, H, Tk, D, elem), contiguous(workspace, 2 * rb)};
   if (!views_ok(outs, 4, ins, 6)) return GPTATTN_ERROR_INVALID_VALUE;
-  if (!workspace || !aligned(workspace) || workspace_bytes < rb) return GPTATTN_ERROR_WORKSPACE;
+  if (!workspace || !aligned(workspace) || workspace_bytes < 2 * rb)
+    return GPTATTN_ERROR_WORKSPACE;
   const bool f32 = elem == 4;
   float* delta = static_cast<float*>(workspace);
   const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -475,13 +478,13 @@ GPTATTN_API size_t gptattn_bwd_ex_workspace_bytes(const gptattn_problem* p) {
   size_t elem = 0;
   bool head_ok = false;
   if (check_problem(p, &elem, &head_ok) != GPTATTN_SUCCESS) return 0;
-  return (size_t)p->B * p->H * p->Tq * 4;
+  return (size_t)p->B * p->H * p->Tq * 8;
 }
 
 GPTATTN_API size_t gptattn_bwd_workspace_bytes(int B, int H, int T, int D, int is_f32) {
   size_t tb = 0, rb = 0;
   if (!sizes(B, H, T, D, is_f32 ? 4 : 2, &tb, &rb)) return 0;
-  return rb;
+  return 2 * rb;
 }
 
 GPTATTN_API const char* gptattn_status_string(int status) {

@@ -40,6 +40,13 @@ hipError_t launch_bwd_dkdv_bf16(const TensorArg& q, const TensorArg& k, const Te
                                 const TensorArg& dk, const TensorArg& dv, const ProblemArg& p,
                                 hipStream_t stream);
 
+// Head size 64 without dropout: the software-pipelined kernels
+// (attn_d64.hip); the bf16 launchers route such problems there themselves.
+hipError_t launch_bwd_dkdv_d64(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                               const TensorArg& dO, const float* lse, const float* delta,
+                               const TensorArg& dk, const TensorArg& dv, const ProblemArg& p,
+                               hipStream_t stream);
+
 // Short query blocks (Tq <= 4, Tk >= 64, no dropout, bf16): one workgroup per
 // head streams the keys (attn_decode.hip).  launch_fwd_bf16 routes such
 // problems here itself.

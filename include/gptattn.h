@@ -108,11 +108,12 @@ int gptattn_bwd(const void* q, const void* k, const void* v, const void* o,
  * each kernel).  gptattn_bwd == gptattn_bwd_dq followed, on the same stream,
  * by gptattn_bwd_dkdv with the same workspace.
  *
- * gptattn_bwd_dq writes dq and stores the row term sum_d dO O (B*H*T
- * float32) in `workspace`.  gptattn_bwd_dkdv reads that row term from
- * `workspace` (which must hold the values gptattn_bwd_dq stored for the
- * same inputs, on the same stream or after synchronising) and writes dk, dv.
- * Arguments as for gptattn_bwd.
+ * gptattn_bwd_dq writes dq and stores per-query values in `workspace` (two
+ * [B][H][T] float32 vectors; bf16 entry points: minus the row term
+ * sum_d dO O, then -lse/scale; float32 entry points: the row term).
+ * gptattn_bwd_dkdv reads them from `workspace` (which must hold the values
+ * gptattn_bwd_dq stored for the same inputs, on the same stream or after
+ * synchronising) and writes dk, dv.  Arguments as for gptattn_bwd.
  */
 int gptattn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
                    const void* dO, const float* lse, void* dq, int B, int H,
@@ -150,7 +151,7 @@ int gptattn_bwd_dkdv_f32(const float* q, const float* k, const float* v,
 /*
  * Bytes of device workspace gptattn_bwd / gptattn_bwd_f32 need for the given
  * shape (is_f32 selects the float32 entry point); 0 if the shape is invalid.
- * Holds the float32 row term sum_d dO O, B*H*T values.
+ * Holds two float32 vectors of B*H*T per-query values (see gptattn_bwd_dq).
  */
 size_t gptattn_bwd_workspace_bytes(int B, int H, int T, int D, int is_f32);
 
@@ -255,7 +256,8 @@ int gptattn_bwd_ex(const gptattn_problem* p, const gptattn_tensor* q,
                    const gptattn_tensor* dk, const gptattn_tensor* dv,
                    void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes for gptattn_bwd_ex (B*H*Tq float32); 0 if p is invalid. */
+/* Workspace bytes for gptattn_bwd_ex (two B*H*Tq float32 vectors); 0 if p is
+ * invalid. */
 size_t gptattn_bwd_ex_workspace_bytes(const gptattn_problem* p);
 
 /* Static, human-readable text for a status code (never NULL). */

@@ -53,8 +53,8 @@ def test_version_and_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert G.workspace_bytes(12, 12, 1024, 64) == 12 * 12 * 1024 * 4
-    assert G.workspace_bytes(1, 4, 64, 16, True) == 4 * 64 * 4
+    assert G.workspace_bytes(12, 12, 1024, 64) == 2 * 12 * 12 * 1024 * 4
+    assert G.workspace_bytes(1, 4, 64, 16, True) == 2 * 4 * 64 * 4
     assert G.workspace_bytes(0, 1, 1, 64) == 0
     assert G.workspace_bytes(1, 1, -3, 64) == 0
 
@@ -156,7 +156,7 @@ def test_unsupported_head_size(lib, D, f32):
 
 def test_workspace_checks(lib):
     assert bwd(lib, ws=0) == WORKSPACE
-    assert bwd(lib, ws_bytes=8 * 4 - 1) == WORKSPACE  # needs B*H*T*4 = 32 bytes
+    assert bwd(lib, ws_bytes=2 * 8 * 4 - 1) == WORKSPACE  # needs 2*B*H*T*4 = 64 bytes
 
 
 def test_overlapping_outputs(lib):

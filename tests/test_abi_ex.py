@@ -57,7 +57,7 @@ def dense_outs(p):
 
 def test_workspace_bytes_ex(lib):
     p = prob(B=3, H=5, Tq=7, Tk=40)
-    assert lib.gptattn_bwd_ex_workspace_bytes(ctypes.byref(p)) == 3 * 5 * 7 * 4
+    assert lib.gptattn_bwd_ex_workspace_bytes(ctypes.byref(p)) == 2 * 3 * 5 * 7 * 4
     assert lib.gptattn_bwd_ex_workspace_bytes(None) == 0
     assert lib.gptattn_bwd_ex_workspace_bytes(ctypes.byref(prob(Tq=0))) == 0
 
