@@ -269,6 +269,20 @@ def _tensor(t):
     return Tensor(t.data_ptr(), st[0], st[1], st[2])
 
 
+def _view_ok(t):
+    """Whether the strided calls take ``t`` as it is: 16-byte aligned data,
+    a contiguous last dimension, non-negative strides that are whole 16-byte
+    units, rows that do not overlap (row stride >= D unless there is a
+    single row) and row strides of at most 2^23 elements.  Autograd can hand
+    the backward pass a gradient that fails this (``o.sum(dim=2)`` gives
+    dO a row stride of 0); such a tensor is copied first."""
+    unit = 16 // t.element_size()
+    st = [0 if t.shape[i] == 1 else t.stride(i) for i in range(3)]
+    return (t.data_ptr() % 16 == 0 and t.stride(3) == 1 and all(s >= 0 for s in st)
+            and all(s % unit == 0 for s in st)
+            and (t.shape[2] == 1 or t.stride(2) >= t.shape[3]) and st[2] <= (1 << 23))
+
+
 def _problem(q, k, scale, causal_offset, window, dropout=0.0, seed=0, rng_stream=0):
     B, H, Tq, D = q.shape
     dt = DTYPE_F32 if q.dtype == torch.float32 else DTYPE_BF16
@@ -367,7 +381,7 @@ class GPTAttnFunction(torch.autograd.Function):
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        if do.stride(3) != 1:
+        if not _view_ok(do):
             do = do.contiguous()
         dq, dk, dv = bwd_ex(q, k, v, o, do, lse, *ctx.args, **ctx.drop)
         return dq, dk, dv, None, None, None, None, None, None

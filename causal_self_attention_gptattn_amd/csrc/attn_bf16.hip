@@ -296,7 +296,7 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
         }
         if (DROP) {
           // dp holds dO.V - delta; the dropped-out weight's gradient is
-          // M / (1 - p) * dO.V, so dS = P * (M / (1 - p) * dO.V - delta)
+          // M * s * dO.V (s: the keep scale), so dS = P * (M * s * dO.V - delta)
           const float delta = -nd[0];
           const bool keep = ((j < 4 ? kb0 : kb1) >> (j & 3)) & 1u;
           ds[j] = p * (keep ? __builtin_fmaf(dp[r] + delta, pb.inv_keep, -delta) : -delta);
@@ -901,7 +901,10 @@ Problem make_problem(const ProblemArg& p) {
   if (p.dropout > 0.0f) {
     const double t = ceil((double)p.dropout * 65536.0);
     pb.thr = t >= 65536.0 ? 65536u : (uint32_t)t;
-    pb.inv_keep = 1.0f / (1.0f - p.dropout);
+    // kept weights are scaled by the inverse of the realised keep
+    // probability (2^16 - thr) / 2^16, so the dropped-out weights stay
+    // unbiased (all dropped when thr = 2^16: the scale is never used)
+    pb.inv_keep = pb.thr >= 65536u ? 0.0f : (float)(65536.0 / (65536.0 - (double)pb.thr));
   }
   return pb;
 }

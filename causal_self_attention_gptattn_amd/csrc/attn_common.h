@@ -137,11 +137,12 @@ struct Problem {
   uint32_t seed_lo, seed_hi;  // Philox key
   uint32_t stream;            // fourth counter word
   uint32_t thr;               // drop iff 16-bit draw < thr, thr = ceil(p * 2^16)
-  float inv_keep;             // 1 / (1 - p)
+  float inv_keep;             // keep scale 2^16 / (2^16 - thr)
 };
 
 // Kernel-side problem description from the host-side one (launch.h); fills
-// the dropout threshold thr = ceil(p * 2^16) and 1 / (1 - p).
+// the dropout threshold thr = ceil(p * 2^16) and the keep scale
+// 2^16 / (2^16 - thr).
 struct ProblemArg;
 Problem make_problem(const ProblemArg& p);
 
@@ -199,7 +200,8 @@ __device__ __forceinline__ int queries_hi(int j1, const Problem& pb) {
 // with key (seed_lo, seed_hi); the draw is the low half of word j % 4 for
 // even i and its high half for odd i.  The weight is kept iff draw >= thr
 // (thr = ceil(p * 2^16), so it is dropped with probability thr / 2^16) and
-// then scaled by 1 / (1 - p).
+// then scaled by 2^16 / (2^16 - thr), the inverse of the realised keep
+// probability, so that the expected scaled weight is the weight itself.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
                                                uint32_t c3, uint32_t k0, uint32_t k1) {

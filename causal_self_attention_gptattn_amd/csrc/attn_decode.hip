@@ -188,8 +188,12 @@ View view(const TensorArg& t) {
 
 // Short query blocks against at least one full key tile: below that the
 // tile kernel is just as fast and keeps its exact arithmetic.
+// One workgroup of kDecThreads work-items per head: the dispatch counts
+// work-items in 32 bits, so more than 2^32 / kDecThreads heads go to the
+// tile kernel instead.
 bool decode_applies(const ProblemArg& p) {
-  return p.Tq <= kDecQ && p.Tk >= 64 && p.dropout <= 0.0f && (p.D == 64 || p.D == 128);
+  return p.Tq <= kDecQ && p.Tk >= 64 && p.dropout <= 0.0f && (p.D == 64 || p.D == 128) &&
+         (long long)p.B * p.H * kDecThreads < (1LL << 32);
 }
 
 hipError_t launch_decode_bf16(const TensorArg& q, const TensorArg& k, const TensorArg& v,

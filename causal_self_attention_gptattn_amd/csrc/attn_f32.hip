@@ -49,7 +49,7 @@ __device__ __forceinline__ void key_range(int i, const Problem& pb, int& lo, int
   hi = i < pb.Tq ? keys_hi(i, pb) : -1;
 }
 
-// Dropout factor of (query i, key j): 0 or 1 / (1 - p); `bits` caches the
+// Dropout factor of (query i, key j): 0 or the keep scale 2^16 / (2^16 - thr); `bits` caches the
 // keep bits of the call covering j's group of four keys (and query i's
 // pair), drawn when j starts a group.
 template <bool DROP>

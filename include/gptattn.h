@@ -191,8 +191,8 @@ size_t gptattn_bwd_workspace_bytes(int B, int H, int T, int D, int is_f32);
  *    contributes no gradient.
  *
  * 3. Dropout.  With dropout = p > 0 the softmax weights are dropped with
- *    probability p and the kept ones scaled by 1/(1 - p) before they weight
- *    the values (lecture chapter "scaling up the model! ... adding dropout";
+ *    probability p and the kept ones scaled by the inverse of the keep
+ *    probability before they weight the values (lecture chapter "scaling up the model! ... adding dropout";
  *    nanoGPT README's --dropout flag); lse stays the softmax's own
  *    normaliser.  The keep mask is not stored: every kernel redraws it from
  *    Philox4x32-10 (Salmon et al., "Parallel Random Numbers: As Easy as 1,
@@ -200,10 +200,13 @@ size_t gptattn_bwd_workspace_bytes(int B, int H, int T, int D, int is_f32);
  *    generator runs on counter (j / 4, i / 2, n, rng_stream) with key
  *    (seed & 0xffffffff, seed >> 32); the draw is the low 16 bits of output
  *    word j % 4 for even i and its high 16 bits for odd i, and the weight is
- *    kept iff draw >= ceil(p * 2^16).  The same problem (seed, rng_stream,
- *    p) must be passed to the forward and backward calls.
+ *    kept iff draw >= thr = ceil(p * 2^16).  The keep probability realised
+ *    is then (2^16 - thr) / 2^16, and kept weights are scaled by
+ *    2^16 / (2^16 - thr), so the dropped-out weights are unbiased.  The
+ *    same problem (seed, rng_stream, p) must be passed to the forward and
+ *    backward calls.
  *
- * lse and the workspace stay dense: [B][H][Tq] float32.
+ * lse is dense: [B][H][Tq] float32; the workspace holds two such vectors.
  * ------------------------------------------------------------------------ */
 
 enum gptattn_dtype {

@@ -12,7 +12,7 @@ lecture description page in its own order:
   the affinity-weighted sum of values;
 * chapter "version 3: adding softmax": the weights are a row softmax of the
   masked affinities;
-* correction at 00:57:00: tokens from the *future* cannot communicate, so a
+* correction at 00:57:00: a query never looks at later positions, so a
   query at position i sees keys j <= i (its own position included, as in the
   "version 1: averaging past context" chapter);
 * note 6 and the correction at 01:20:05: affinities are scaled by
@@ -22,9 +22,12 @@ lecture description page in its own order:
   and note 3 says batch elements never communicate;
 * chapter "scaling up the model! ... adding dropout" (with the nanoGPT
   README's `--dropout` flag): optional dropout on the attention weights.
-  Read as: the softmax weights P are multiplied by a keep mask M and by
-  1 / (1 - p) before they weight the values; lse is the normaliser of the
-  softmax itself, before dropout.  M comes from oracle.philox.keep_mask.
+  Read as: the softmax weights P are multiplied by a keep mask M and by the
+  keep scale s = 2^16 / (2^16 - thr) (the inverse of the keep probability
+  the generator's 16-bit threshold thr = ceil(p * 2^16) realises, so the
+  dropped-out weights are unbiased) before they weight the values; lse is
+  the normaliser of the softmax itself, before dropout.  M comes from
+  oracle.philox.keep_mask, s from oracle.philox.keep_scale.
 
 Layout: every tensor is ``[B, H, T, D]`` (``lse`` is ``[B, H, T]``).  Inputs
 of any float dtype are upcast exactly to float64; ``scale`` is taken as the
@@ -39,8 +42,8 @@ scalar loss L = sum(O * dO), so dL/dO = dO:
     dQ = scale * dS K
     dK = scale * dS^T Q
 
-With dropout, Pd = P * M / (1 - p) replaces P in O = Pd V and dV = Pd^T dO,
-and dP = (dO V^T) * M / (1 - p) enters the softmax Jacobian.
+With dropout, Pd = P * M * s replaces P in O = Pd V and dV = Pd^T dO,
+and dP = (dO V^T) * M * s enters the softmax Jacobian.
 """
 
 import numpy as np
@@ -112,10 +115,12 @@ def probabilities(q, k, scale, offset=0, window=0):
 
 
 def _drop_factor(keep, p):
-    """Per-weight dropout factor M / (1 - p) (all ones without dropout)."""
+    """Per-weight dropout factor M * s (None without dropout), s the keep
+    scale of oracle.philox.keep_scale: the inverse of the keep probability
+    the generator's threshold realises."""
     if keep is None:
         return None
-    return keep.astype(np.float64) / (1.0 - float(np.float32(p)))
+    return keep.astype(np.float64) * philox.keep_scale(p)
 
 
 def forward_head(q, k, v, scale, offset=0, window=0, keep=None, p=0.0):

@@ -16,10 +16,13 @@ Inputs are nested lists indexed ``[b][h][t][d]``; so are the outputs
 (``lse`` is ``[b][h][t]``).  The optional ``offset`` and ``window`` select
 which keys a query sees exactly as in :func:`oracle.attention.visible`.
 ``keep`` (nested ``[b][h][i][j]`` booleans) and ``drop`` apply dropout to
-the weights: a kept weight is divided by 1 - drop, a dropped one is 0.
+the weights: a dropped weight is 0, a kept one is multiplied by the inverse
+of the keep probability the 16-bit draws realise, 2^16 / (2^16 - thr) with
+thr = ceil(p * 2^16) for the float32 value p of ``drop``.
 """
 
 import math
+import struct
 
 
 def _keys(i, Tk, offset, window):
@@ -30,10 +33,18 @@ def _keys(i, Tk, offset, window):
     return list(range(lo, hi + 1))
 
 
+def _keep_scale(drop):
+    """2^16 / (2^16 - thr): a draw x in 0 .. 2^16 - 1 keeps the weight iff
+    x >= thr, so 2^16 - thr of the 2^16 draws keep it."""
+    p32 = struct.unpack("<f", struct.pack("<f", drop))[0]
+    thr = min(math.ceil(p32 * 65536.0), 65536) if p32 > 0 else 0
+    return 65536.0 / (65536 - thr) if thr < 65536 else 0.0
+
+
 def _factor(keep, i, j, drop):
     if keep is None:
         return 1.0
-    return (1.0 / (1.0 - drop)) if keep[i][j] else 0.0
+    return _keep_scale(drop) if keep[i][j] else 0.0
 
 
 def _head_forward(q, k, v, scale, offset=0, window=0, keep=None, drop=0.0):

@@ -21,8 +21,11 @@ head-problem n = b * H + h, query i and key j, the generator runs on counter
 (j // 4, i // 2, n, stream) with key (seed & 0xffffffff, seed >> 32); the
 draw x is the low 16 bits of output word j % 4 for even i and its high 16
 bits for odd i.  The weight is kept iff x >= thr, thr = ceil(p * 2^16) (so it
-is dropped with probability thr / 2^16), and a kept weight is scaled by
-1 / (1 - p).
+is dropped with probability thr / 2^16), and a kept weight is scaled by the
+inverse of the keep probability so realised, 2^16 / (2^16 - thr): over the
+2^16 equally likely draws the scaled keep factor then averages to exactly 1
+(dropout leaves the expected weights unchanged; with 1 / (1 - p) the
+rounding of p * 2^16 up to thr would leave a bias of up to 2^-16 / (1 - p)).
 """
 
 import numpy as np
@@ -58,6 +61,13 @@ def threshold(p):
     p in [0, 1)."""
     p = float(np.float32(p))
     return min(int(np.ceil(p * 2.0 ** 16)), 2 ** 16) if p > 0 else 0
+
+
+def keep_scale(p):
+    """Factor of a kept weight: 2^16 / (2^16 - thr), the inverse of the keep
+    probability the threshold realises (0 when every weight is dropped)."""
+    thr = threshold(p)
+    return 0.0 if thr >= 2 ** 16 else 2.0 ** 16 / (2 ** 16 - thr)
 
 
 def keep_mask(n, Tq, Tk, p, seed, stream=0):

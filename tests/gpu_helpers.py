@@ -10,11 +10,17 @@ import torch
 import causal_self_attention_gptattn_amd as G
 from oracle import attention as A
 
-# Tolerances, per element |gpu - oracle| <= abs + rel_elem * |oracle|:
+# Tolerances, per element |gpu - oracle| <= abs (+ rel_elem * |oracle| where
+# |oracle| >= rel_from):
 #   bf16: abs 2e-2 on outputs and gradients plus one bf16 unit round-off
-#         (2^-8) of the value itself -- a bf16 result of magnitude >= 8 is
-#         only representable to within 2^-5, so a pure 2e-2 bound would be
-#         below the storage format's own resolution there.  On top of that a
+#         (2^-8) of the value itself.  An output is formed from bf16 weights
+#         (2^-9 of each term), normalised by the float32 sum of the unrounded
+#         weights (another 2^-9 when one weight dominates) and stored in bf16
+#         (2^-9 of itself), so with peaked weights its storage roundings
+#         alone reach about 2^-7.4 |O|, above the plain 2e-2 from |O| ~ 3.4
+#         on (measured on the GPT-3-shaped layer with a 256-wide band:
+#         2.3e-2 at |O| = 3.55, 3.8e-2 at |O| = 7.8).  compare() reports how
+#         many elements needed the extra term.  On top of that a
 #         relative Frobenius bound of 1e-2 per tensor pins small gradients
 #         (2e-2 absolute alone would accept an all-zero dQ).  lse (float32
 #         in both precisions) 1e-3 absolute.
@@ -24,9 +30,13 @@ from oracle import attention as A
 #         such roundings relative to the terms, so a gradient of magnitude 15
 #         summed over 500 queries can sit 1.5e-5 from the float64 value;
 #         2^-20 is 16 units in the last place.  lse 1e-5 absolute.
+#   The tiny float32 workload (values O(1)) is held to the plain 1e-5
+#   (strict=True in compare).
 TOL = {
-    "bf16": {"abs": 2e-2, "rel_elem": 2.0 ** -8, "rel_fro": 1e-2, "lse": 1e-3},
-    "f32": {"abs": 1e-5, "rel_elem": 2.0 ** -20, "rel_fro": 1e-5, "lse": 1e-5},
+    "bf16": {"abs": 2e-2, "rel_elem": 2.0 ** -8, "rel_from": 0.0, "rel_fro": 1e-2,
+             "lse": 1e-3},
+    "f32": {"abs": 1e-5, "rel_elem": 2.0 ** -20, "rel_from": 0.0, "rel_fro": 1e-5,
+            "lse": 1e-5},
 }
 
 
@@ -69,7 +79,7 @@ def rounding_bound(inp, offset=0, window=0, dropout=0.0, seed=0, stream=0):
     dS K and dS^T Q, the row term delta formed from the bf16-stored O, and
     every output rounded once.  Float64, oracle side.  The sweep and dropout
     tests draw iid N(0, 1) data (gradients 100x the workloads', whose dO is
-    N(0, 0.01)) and amplify kept weights by 1 / (1 - p); there the storage
+    N(0, 0.01)) and amplify kept weights by about 1 / (1 - p); there the storage
     floor alone can exceed the fixed 2e-2, and this bound is the yardstick.
     The bound is worst-case: measured errors sit well inside it."""
     from oracle import philox
@@ -85,7 +95,7 @@ def rounding_bound(inp, offset=0, window=0, dropout=0.0, seed=0, stream=0):
             f = 1.0
             if dropout > 0:
                 keep = philox.keep_mask(b * H + h, Tq, kh.shape[0], dropout, seed, stream)
-                f = keep.astype(np.float64) / (1.0 - float(np.float32(dropout)))
+                f = keep.astype(np.float64) * philox.keep_scale(dropout)
             pd = p * f
             o = pd @ vh
             ds = p * ((dh @ vh.T) * f - (dh * o).sum(axis=1, keepdims=True))
@@ -99,10 +109,13 @@ def rounding_bound(inp, offset=0, window=0, dropout=0.0, seed=0, stream=0):
     return out
 
 
-def compare(got, ref, dtype, heads=None, label="", bound=None):
+def compare(got, ref, dtype, heads=None, label="", bound=None, strict=False):
     """Assert parity on all heads or on the listed (b, h) heads.  With
     `bound` (rounding_bound, all heads), an element also passes when its
-    error lies within that bound."""
+    error lies within that bound.  strict: the plain absolute gate only.
+    Prints, per tensor, the max abs error, the relative Frobenius error and
+    the number of elements beyond the plain absolute gate (each of which
+    passed on the relative term or the bound)."""
     tol = TOL[dtype]
     report = {}
     for name in ("o", "lse", "dq", "dk", "dv"):
@@ -120,11 +133,16 @@ def compare(got, ref, dtype, heads=None, label="", bound=None):
         err = diff.max()
         rnorm = np.linalg.norm(r)
         rel = np.linalg.norm(g - r) / rnorm if rnorm > 0 else 0.0
-        report[name] = (err, rel)
+        beyond = int((diff > tol["abs"]).sum()) if name != "lse" else 0
+        report[name] = (err, rel, beyond)
         if name == "lse":
             assert err <= tol["lse"], "%s lse: max abs err %.3e > %.1e" % (label, err, tol["lse"])
             continue
-        lim = tol["abs"] + tol["rel_elem"] * np.abs(r)
+        if strict:
+            lim = np.full_like(r, tol["abs"])
+        else:
+            lim = tol["abs"] + np.where(np.abs(r) >= tol["rel_from"],
+                                        tol["rel_elem"] * np.abs(r), 0.0)
         if bound is not None:
             bd = bound[name]
             if heads is not None:
@@ -139,7 +157,8 @@ def compare(got, ref, dtype, heads=None, label="", bound=None):
         if rnorm > 0:
             assert rel <= tol["rel_fro"], "%s %s: rel Frobenius err %.3e > %.1e" % (
                 label, name, rel, tol["rel_fro"])
-    say(label, " ".join("%s=%.2e/%.2e" % (n, e, r) for n, (e, r) in report.items()))
+    say(label, "max-abs/rel-Frobenius/beyond-plain:",
+        " ".join("%s=%.2e/%.2e/%d" % (n, e, r, k) for n, (e, r, k) in report.items()))
     return report
 
 

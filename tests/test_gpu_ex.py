@@ -242,3 +242,51 @@ def test_max_row_stride(dtype, D):
         assert torch.equal(a.contiguous(), b)
     got = {"o": to64(o), "lse": to64(lse), "dq": to64(dq), "dk": to64(dk), "dv": to64(dv)}
     compare(got, run_oracle(inp), dtype, label="row stride 2^23 %s D=%d" % (dtype, D))
+
+
+
+def test_autograd_with_a_gradient_pooled_over_positions():
+    """A loss that pools O over positions (here a weighted sum over t) hands
+    the backward pass a dO whose row stride is 0; the wrapper copies it into
+    a layout the strided call takes and the gradients match the oracle's for
+    the same, materialised dO."""
+    dev = need_gpu()
+    B, H, T, D = 2, 3, 150, 64
+    inp = W.make_inputs(B, H, T, D, "bf16", seed=17)
+    q, k, v = (inp[n].to(dev).requires_grad_(True) for n in ("q", "k", "v"))
+    wt = (torch.randn(B, H, D, generator=torch.Generator().manual_seed(3)) * 0.01)
+    wt = wt.to(torch.bfloat16)
+    o = G.attention(q, k, v, inp["scale"])
+    (o.sum(dim=2) * wt.to(dev)).sum().backward()
+    torch.cuda.synchronize()
+    pooled = dict(inp)
+    pooled["do"] = wt[:, :, None, :].expand(B, H, T, D).contiguous()
+    ref = run_oracle(pooled)
+    got = {"o": to64(o), "lse": ref["lse"], "dq": to64(q.grad), "dk": to64(k.grad),
+           "dv": to64(v.grad)}
+    compare(got, ref, "bf16", label="pooled-gradient autograd")
+
+def test_decode_beyond_the_decode_grid_runs_on_the_tile_kernel():
+    """2^22 + 1 heads with one query each are more heads than a decoding
+    launch can count (one workgroup of 1024 work-items per head, 2^32
+    work-items at most), so the call takes the tile kernel instead.  All
+    heads share one query row and one 64-key context (stride-0 views), so
+    every output row must equal the oracle's single row."""
+    from oracle import attention as A
+
+    dev = need_gpu()
+    H = (1 << 22) + 1
+    say("decode beyond the decode grid", 1, H, 1, 64, 63, 0, 64)
+    inp = shifted_inputs(1, 1, 1, 64, 64, "bf16", seed=5)
+    q = inp["q"].to(dev).expand(1, H, 1, 64)
+    k = inp["k"].to(dev).expand(1, H, 64, 64)
+    v = inp["v"].to(dev).expand(1, H, 64, 64)
+    o, lse = G.fwd_ex(q, k, v, inp["scale"], 63, 0)
+    torch.cuda.synchronize()
+    ro, rl = A.forward(*(inp[n].double().numpy() for n in ("q", "k", "v")), inp["scale"],
+                       offset=63)
+    ref_o = torch.from_numpy(ro[0, 0, 0]).to(dev)
+    err_o = float((o[0, :, 0].double() - ref_o).abs().max())
+    err_l = float((lse[0, :, 0].double() - float(rl[0, 0, 0])).abs().max())
+    print("decode beyond the decode grid: max|O err| %.2e, max|lse err| %.2e" % (err_o, err_l))
+    assert err_o <= 2e-2 and err_l <= 1e-3

@@ -46,6 +46,28 @@ def test_threshold():
     assert P.threshold(float(np.nextafter(np.float32(1), np.float32(0)))) == 2 ** 16
 
 
+@pytest.mark.parametrize("p", [0.1, 0.3, 0.5, 0.9, 1e-5, 0.999])
+def test_keep_scale_averages_to_one_over_all_draws(p):
+    """The kept-weight factor is the inverse of the keep probability the
+    16-bit threshold realises: over the 2^16 equally likely draws, the mean of
+    keep * scale is 1 (the dropped-out weights are unbiased).  With the
+    nominal 1 / (1 - p) instead, p = 0.1 (thr rounded up from 6553.6) misses
+    by 6e-6."""
+    thr = P.threshold(p)
+    draws = np.arange(2 ** 16)
+    mean = ((draws >= thr) * P.keep_scale(p)).mean()
+    assert abs(mean - 1.0) <= 1e-15
+    assert P.keep_scale(p) == 2.0 ** 16 / (2 ** 16 - thr)
+    # the scalar-loop twin computes the same factor on its own
+    assert BF._keep_scale(p) == P.keep_scale(p)
+
+
+def test_keep_scale_when_everything_is_dropped():
+    p = float(np.nextafter(np.float32(1), np.float32(0)))
+    assert P.threshold(p) == 2 ** 16 and P.keep_scale(p) == 0.0
+    assert BF._keep_scale(p) == 0.0
+
+
 @pytest.mark.parametrize("p", [0.1, 0.5, 0.9])
 def test_drop_rate_is_binomial(p):
     m = P.keep_mask(3, 256, 512, p, seed=1234, stream=7)
