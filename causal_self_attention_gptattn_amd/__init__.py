@@ -33,7 +33,7 @@ import os
 import torch
 
 __all__ = [
-    "fwd", "bwd", "bwd_dq", "bwd_dkdv", "fwd_ex", "bwd_ex", "split_qkv", "attention",
+    "fwd", "bwd", "bwd_noalloc", "bwd_dq", "bwd_dkdv", "fwd_ex", "bwd_ex", "split_qkv", "attention",
     "GPTAttnFunction", "workspace_bytes", "ex_workspace_bytes", "status_string", "version",
     "library", "LIB_PATH", "Tensor", "Problem", "DTYPE_BF16", "DTYPE_F32",
 ]
@@ -73,6 +73,7 @@ _pp = ctypes.POINTER(Problem)
 SIGNATURES = {
     "gptattn_fwd": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p]),
     "gptattn_bwd": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p, _sz, _p]),
+    "gptattn_bwd_noalloc": (_i, [_p, _p, _p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p]),
     "gptattn_bwd_dq": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p, _sz, _p]),
     "gptattn_bwd_dkdv": (_i, [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p, _sz, _p]),
     "gptattn_fwd_f32": (_i, [_p, _p, _p, _p, _p, _i, _i, _i, _i, _f, _p]),
@@ -194,6 +195,29 @@ def bwd(q, k, v, o, do, lse, scale=None, dq=None, dk=None, dv=None, workspace=No
                 workspace.numel() * workspace.element_size(), _stream(q.device))
     _check(rc, "gptattn_bwd")
     return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, do, lse, scale=None, dq=None, dk=None, dv=None):
+    """Backward pass (bfloat16) through ``gptattn_bwd_noalloc``: no
+    workspace; the library's fixed scratch array takes its place (at most
+    ``NOALLOC_MAX_ROWS`` = B*H*T rows; overlapping calls on one GPU race)."""
+    _validate(q, k, v, o, do)
+    B, H, T, D = q.shape
+    if lse.shape != (B, H, T) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _validate(q, dq, dk, dv)
+    with torch.cuda.device(q.device):
+        rc = library().gptattn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do),
+                                           _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), B, H, T, D,
+                                           _scale(scale, D), _stream(q.device))
+    _check(rc, "gptattn_bwd_noalloc")
+    return dq, dk, dv
+
+
+NOALLOC_MAX_ROWS = 1 << 20
 
 
 def _rows_ok(t, q):

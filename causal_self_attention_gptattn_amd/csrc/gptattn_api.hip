@@ -5,6 +5,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gptattn.h"
 #include "launch.h"
 
@@ -90,7 +92,7 @@ struct Buf {
 
 int check_bwd(const Buf* ins, int nin, const Buf* outs, int nout, const void* ws,
               size_t ws_bytes, bool ws_is_output, int B, int H, int T, int D, float scale,
-              size_t elem, bool head_ok) {
+              size_t elem, bool head_ok, bool has_ws = true) {
   size_t tb = 0, rb = 0;
   for (int i = 0; i < nin; ++i)
     if (!ins[i].p || !aligned(ins[i].p)) return GPTATTN_ERROR_INVALID_VALUE;
@@ -101,12 +103,13 @@ int check_bwd(const Buf* ins, int nin, const Buf* outs, int nout, const void* ws
   if (!head_ok) return GPTATTN_ERROR_NOT_SUPPORTED;
   // the workspace holds two [B][H][T] float vectors (see include/gptattn.h)
   const size_t wb = 2 * rb;
-  if (!ws || !aligned(ws) || ws_bytes < wb) return GPTATTN_ERROR_WORKSPACE;
+  if (has_ws && (!ws || !aligned(ws) || ws_bytes < wb)) return GPTATTN_ERROR_WORKSPACE;
   Range ri[8], ro[8];
   int ni = 0, no = 0;
   for (int i = 0; i < nin; ++i) ri[ni++] = rng(ins[i].p, ins[i].rows ? rb : tb);
   for (int i = 0; i < nout; ++i) ro[no++] = rng(outs[i].p, outs[i].rows ? rb : tb);
-  if (ws_is_output) {
+  if (!has_ws) {
+  } else if (ws_is_output) {
     ro[no++] = rng(ws, wb);
   } else {
     ri[ni++] = rng(ws, wb);
@@ -364,6 +367,65 @@ GPTATTN_API int gptattn_bwd(const void* q, const void* k, const void* v, const v
                    workspace_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// Backward pass without a workspace argument and without allocating: the
+// per-query values gptattn_bwd keeps in its workspace (two float vectors of
+// B*H*T) live in `scratch`, a device array of fixed size.  Each GPU holds its
+// own copy; its address is looked up once per device, with that device
+// current, and kept in g_scratch (the array's name in host code is only a
+// host-side stand-in, never a device address).  Calls on one GPU share that
+// GPU's copy, so calls whose executions overlap on one GPU race.  Nothing in
+// it needs to start at zero: the dQ launch writes every value the dK/dV
+// launch reads.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr long long kNoallocRows = GPTATTN_NOALLOC_MAX_ROWS;
+static __device__ __align__(256) float scratch[2 * kNoallocRows];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices];
+
+// This device's copy of the scratch array (nullptr on failure).
+void* scratch_on(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+}  // namespace
+
+GPTATTN_API int gptattn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                    const void* dO, const float* lse, void* dq, void* dk,
+                                    void* dv, int B, int H, int T, int D, float scale,
+                                    void* stream) {
+  const Buf ins[6] = {{q, false}, {k, false}, {v, false}, {o, false}, {dO, false}, {lse, true}};
+  const Buf outs[3] = {{dq, false}, {dk, false}, {dv, false}};
+  const int st = check_bwd(ins, 6, outs, 3, nullptr, 0, true, B, H, T, D, scale, 2,
+                           bf16_head_ok(D), false);
+  if (st != GPTATTN_SUCCESS) return st;
+  if ((long long)B * H * T > kNoallocRows) return GPTATTN_ERROR_SCRATCH;
+  // the scratch copy of the device the stream belongs to, which must be the
+  // current device (the library never changes it)
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  int dev = -1, sdev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return GPTATTN_ERROR_LAUNCH;
+  if (s && (hipStreamGetDevice(s, &sdev) != hipSuccess || sdev != dev))
+    return GPTATTN_ERROR_INVALID_VALUE;
+  float* delta = static_cast<float*>(scratch_on(dev));
+  if (!delta) return GPTATTN_ERROR_LAUNCH;
+  const ProblemArg p = causal(B, H, T, D, scale);
+  if (dq_any(false, dense(q, H, T, D), dense(k, H, T, D), dense(v, H, T, D), dense(o, H, T, D),
+             dense(dO, H, T, D), lse, dense(dq, H, T, D), delta, p, s) != hipSuccess)
+    return GPTATTN_ERROR_LAUNCH;
+  return launched(dkdv_any(false, dense(q, H, T, D), dense(k, H, T, D), dense(v, H, T, D),
+                           dense(dO, H, T, D), lse, delta, dense(dk, H, T, D),
+                           dense(dv, H, T, D), p, s));
+}
+
 GPTATTN_API int gptattn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
                                const void* dO, const float* lse, void* dq, int B, int H, int T,
                                int D, float scale, void* workspace, size_t workspace_bytes,
@@ -498,6 +560,9 @@ GPTATTN_API const char* gptattn_status_string(int status) {
     case GPTATTN_ERROR_WORKSPACE:
       return "GPTATTN_ERROR_WORKSPACE: workspace missing, misaligned or too small";
     case GPTATTN_ERROR_LAUNCH: return "GPTATTN_ERROR_LAUNCH: kernel launch failed";
+    case GPTATTN_ERROR_SCRATCH:
+      return "GPTATTN_ERROR_SCRATCH: B*H*T exceeds GPTATTN_NOALLOC_MAX_ROWS, the size of "
+             "gptattn_bwd_noalloc's scratch array";
     default: return "GPTATTN: unknown status code";
   }
 }

@@ -32,20 +32,22 @@
  *
  * Ownership and execution: the caller owns every buffer (device memory).
  * The library allocates nothing, frees nothing, never synchronises and never
- * changes the current device; all work is enqueued on `stream`, a
+ * changes the current device (gptattn_bwd_noalloc uses a fixed array of its
+ * own, see there); all work is enqueued on `stream`, a
  * hipStream_t passed as void* (NULL = the default stream), and completes
  * asynchronously.  Outputs are fully overwritten, never accumulated.  Inputs
  * are read only.  Outputs may not overlap the inputs or each other.
  *
  * Errors: every entry point returns 0 (GPTATTN_SUCCESS) or a status code.
  * Arguments are validated before any HIP call, so a call that returns
- * INVALID_VALUE, NOT_SUPPORTED or WORKSPACE has enqueued nothing.
+ * INVALID_VALUE, NOT_SUPPORTED, WORKSPACE or SCRATCH has enqueued nothing.
  * GPTATTN_ERROR_LAUNCH reports a failed kernel launch.  Faults inside a
  * kernel surface at the caller's next synchronisation.  Nothing aborts and
  * no C++ exception crosses this interface.
  *
- * Thread safety: stateless and reentrant; concurrent calls on different
- * streams are safe provided their buffers do not overlap.
+ * Thread safety: stateless and reentrant (except gptattn_bwd_noalloc, whose
+ * overlapping calls on one GPU race); concurrent calls on different streams
+ * are safe provided their buffers do not overlap.
  */
 #ifndef GPTATTN_H
 #define GPTATTN_H
@@ -66,7 +68,9 @@ enum gptattn_status {
   /* backward workspace null or smaller than gptattn_bwd_workspace_bytes() */
   GPTATTN_ERROR_WORKSPACE = 3,
   /* a kernel launch failed (hipLaunchKernel returned an error) */
-  GPTATTN_ERROR_LAUNCH = 4
+  GPTATTN_ERROR_LAUNCH = 4,
+  /* gptattn_bwd_noalloc: B*H*T larger than GPTATTN_NOALLOC_MAX_ROWS */
+  GPTATTN_ERROR_SCRATCH = 5
 };
 
 /* Required alignment, in bytes, of every tensor pointer. */
@@ -101,6 +105,29 @@ int gptattn_bwd(const void* q, const void* k, const void* v, const void* o,
                 const void* dO, const float* lse, void* dq, void* dk,
                 void* dv, int B, int H, int T, int D, float scale,
                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Backward pass, bfloat16 tensors, without a workspace and without any
+ * allocation: for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid it).
+ * Arguments and results as for gptattn_bwd, minus the workspace.  The
+ * per-query values gptattn_bwd keeps in its workspace go to a scratch array
+ * the library holds in device memory: 2 * GPTATTN_NOALLOC_MAX_ROWS float32
+ * (8 MiB) on every GPU it runs on, until the process ends.
+ *   - B*H*T must not exceed GPTATTN_NOALLOC_MAX_ROWS, else
+ *     GPTATTN_ERROR_SCRATCH (checked with the other arguments, before any
+ *     HIP call).
+ *   - `stream` must belong to the current device (else INVALID_VALUE); the
+ *     first call on a device looks up that device's copy of the array.
+ *   - Every call on one GPU uses that GPU's one copy: calls whose executions
+ *     overlap on one GPU (on different streams, or from threads that do not
+ *     order them) race.  The array needs no initial value.
+ */
+#define GPTATTN_NOALLOC_MAX_ROWS 1048576
+int gptattn_bwd_noalloc(const void* q, const void* k, const void* v,
+                        const void* o, const void* dO, const float* lse,
+                        void* dq, void* dk, void* dv, int B, int H, int T,
+                        int D, float scale, void* stream);
 
 /*
  * The backward pass as its two launches, for callers that schedule them

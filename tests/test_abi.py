@@ -13,7 +13,7 @@ import causal_self_attention_gptattn_amd as G
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "gptattn.h")
 
-SUCCESS, INVALID, UNSUPPORTED, WORKSPACE, LAUNCH = 0, 1, 2, 3, 4
+SUCCESS, INVALID, UNSUPPORTED, WORKSPACE, LAUNCH, SCRATCH = 0, 1, 2, 3, 4, 5
 
 
 def declared_functions():
@@ -40,7 +40,7 @@ def test_status_codes_in_header():
     text = open(HEADER).read()
     for name, val in (("GPTATTN_SUCCESS", 0), ("GPTATTN_ERROR_INVALID_VALUE", 1),
                       ("GPTATTN_ERROR_NOT_SUPPORTED", 2), ("GPTATTN_ERROR_WORKSPACE", 3),
-                      ("GPTATTN_ERROR_LAUNCH", 4)):
+                      ("GPTATTN_ERROR_LAUNCH", 4), ("GPTATTN_ERROR_SCRATCH", 5)):
         assert re.search(r"\b%s\s*=\s*%d\b" % (name, val), text), name
 
 
@@ -178,3 +178,28 @@ def test_overlapping_outputs(lib):
     assert bwd(lib, p) == INVALID
     # workspace overlaps lse
     assert bwd(lib, ws=A[5]) == INVALID
+
+
+def bwd_noalloc(lib, ptrs=None, B=1, H=1, T=8, D=64, scale=0.125):
+    p = list(A[:9]) if ptrs is None else ptrs
+    return lib.gptattn_bwd_noalloc(*[ctypes.c_void_p(x) for x in p], B, H, T, D, scale, None)
+
+
+def test_noalloc_rejects_bad_arguments_before_any_hip_call(lib):
+    """The no-allocation backward validates like gptattn_bwd (minus the
+    workspace), and refuses B*H*T beyond its fixed scratch array, all
+    before touching the HIP runtime."""
+    text = open(HEADER).read()
+    limit = int(re.search(r"GPTATTN_NOALLOC_MAX_ROWS\s+(\d+)", text).group(1))
+    assert limit == G.NOALLOC_MAX_ROWS == 1 << 20
+    assert bwd_noalloc(lib, B=1, H=16, T=limit // 16 + 1) == SCRATCH
+    assert bwd_noalloc(lib, B=3, H=(limit + 2) // 3, T=1) == SCRATCH
+    assert bwd_noalloc(lib, D=96) == UNSUPPORTED
+    assert bwd_noalloc(lib, scale=float("nan")) == INVALID
+    p = list(A[:9])
+    p[6] = 0
+    assert bwd_noalloc(lib, p) == INVALID
+    p = list(A[:9])
+    p[7] = p[6]
+    assert bwd_noalloc(lib, p) == INVALID
+    assert "SCRATCH" in G.status_string(SCRATCH)
