@@ -1,8 +1,8 @@
 """Benchmark: causal attention forward + backward on one MI355X.
 
 One step = the whole hot path on one batch: gptattn_fwd (attn_fwd kernel),
-then the backward as its two launches gptattn_bwd_dq (attn_bwd_dq) and
-gptattn_bwd_dkdv (attn_bwd_dkdv), on the GPT-2 124M attention shape
+then the backward as its two launches gptattn_bwd_dq (the dQ kernel) and
+gptattn_bwd_dkdv (the dK/dV kernel), on the GPT-2 124M attention shape
 (B=12, H=12, T=1024, D=64, bf16) with inputs resident in HBM.
 
 Throughput counts algorithmic work only: 6 * D * T * (T + 1) flops per
@@ -10,19 +10,22 @@ head-problem (QK^T and PV forward; dV, dP, dQ, dK backward over the causal
 triangle including the diagonal).  Score recomputation in the backward is
 implementation work and is not counted.
 
-Prints one JSON line.  Per-kernel durations come from HIP events recorded on
-the launch stream around every launch of a separate pass of steps.  Each
-event record costs the stream a few microseconds, so the timed steps carry
-only two per step, around the dominant kernel: its duration for the roofline
-is measured live over the timed steps, and the step-to-step intervals of the
-second event give the per-step spread.
+Timing.  `value` is the cold-cache figure: before every timed step a 1 GiB
+buffer is overwritten (outside the HIP events), which evicts the step's
+227.7 MB working set from the 256 MB last-level cache, so every step reads
+its inputs from HBM.  Each timed step carries three events on the launch
+stream (before the forward, before the dominant kernel, after the step):
+the step time, and the dominant kernel's time for the roofline, both
+measured live over the timed steps.  The warm figure (steps back to back,
+no flush, wall clock) is reported beside it.  A separate pass with an event
+at every launch boundary gives the per-kernel table.
 
-The line also carries "variants": the strided entry points timed the same
-way (HIP events around each step) on the same head shape -- q, k, v read in
-place from a packed [B, T, 3C] buffer with gradients written into one packed
-buffer; a locally banded causal mask of 256 positions; attention dropout with
-p = 0.1; and one decoding step (one query against a 1024-token context,
-forward only, reported in GB/s).
+Prints one JSON line with, besides the contract's keys: the roofline of the
+dominant kernel against whichever of its two roofs (bf16 MFMA, HBM) is the
+tighter one, the measured dense bf16 GEMM rate of the box (the attainable
+matrix-core peak), sclk samples taken while the timed steps run, the CPU
+oracle baseline, the other workloads of the pages (`configs`), and the
+strided entry points (`variants`).
 """
 
 import argparse
@@ -30,7 +33,9 @@ import hashlib
 import json
 import os
 import platform
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -45,7 +50,8 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # / 8 cycles x 2.4 GHz exponentials per second.
 PEAK_EXP_PER_S = 256 * 4 * 64 / 8 * 2.4e9
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gpt2_124m.json")
-KERNEL_SOURCES = ["attn_bf16.hip", "attn_common.h"]
+KERNEL_SOURCES = ["attn_bf16.hip", "attn_d64.hip", "attn_common.h"]
+FLUSH_BYTES = 1 << 30
 
 
 def unit_flops(N, T, D):
@@ -53,11 +59,11 @@ def unit_flops(N, T, D):
     return N * D * T * (T + 1)
 
 
-def kernel_table(N, T, D):
-    """Algorithmic flops, bytes and exponentials per launch of each kernel
-    (bf16).  Each kernel takes one exponential per visible score element."""
+def kernel_table(N, T, D, elem=2):
+    """Algorithmic flops, bytes and exponentials per launch of each kernel.
+    Each kernel takes one exponential per visible score element."""
     u = unit_flops(N, T, D)
-    t = N * T * D * 2      # one bf16 [B,H,T,D] tensor
+    t = N * T * D * elem   # one [B,H,T,D] tensor
     r = N * T * 4          # one float32 [B,H,T] vector
     x = N * T * (T + 1) // 2
     return {
@@ -68,6 +74,21 @@ def kernel_table(N, T, D):
         # dP, dV and dK products; reads Q, K, V, dO, lse, row term, writes dK, dV
         "attn_bwd_dkdv": {"flops": 3 * u, "bytes": 6 * t + 2 * r, "exps": x},
     }
+
+
+def roofline(flops, nbytes, seconds):
+    """The tighter of the two roofs for work (flops, bytes) done in `seconds`:
+    frac = max(F / peak_flops, B / peak_bw) / t.  Reported in the unit of the
+    binding roof."""
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    if t_hbm >= t_mfma:
+        ach = nbytes / seconds / 1e9
+        return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": ach / PEAK_HBM_GBS}
+    ach = flops / seconds / 1e12
+    return {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": ach / PEAK_BF16_TFLOPS}
 
 
 def source_sha():
@@ -106,33 +127,44 @@ def cpu_model():
     return platform.processor() or platform.machine()
 
 
-def clocks_under_load(run_some_steps, limit_s):
-    """sclk and power as rocm-smi reports them while steps keep the GPU busy
-    (best effort: None when the tool is missing or fails)."""
-    import subprocess
+class ClockSampler:
+    """Polls rocm-smi for sclk (and power) in a background thread while the
+    GPU works; best effort (no samples when the tool is missing)."""
 
-    try:
-        proc = subprocess.Popen(["rocm-smi", "--showclocks", "--showpower", "--json"],
-                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
-    except OSError:
-        return None
-    t0 = time.time()
-    while proc.poll() is None and time.time() - t0 < limit_s:
-        run_some_steps()
-    try:
-        out, _ = proc.communicate(timeout=5)
-        rec = json.loads(out)
-    except Exception:  # noqa: BLE001 -- a diagnostic, never fatal
-        proc.kill()
-        return None
-    card = next(iter(rec.values()), {}) if isinstance(rec, dict) else {}
-    keep = {k_: v_ for k_, v_ in card.items()
-            if "sclk" in k_.lower() or "mclk" in k_.lower() or "power" in k_.lower()}
-    return keep or None
+    def __init__(self):
+        self.samples = []
+        self._stop = threading.Event()
+        self._t = None
+
+    def _poll(self):
+        while not self._stop.is_set():
+            try:
+                out = subprocess.run(["rocm-smi", "--showclocks", "--showpower", "--json"],
+                                     capture_output=True, text=True, timeout=10).stdout
+                rec = json.loads(out)
+            except Exception:  # noqa: BLE001 -- a diagnostic, never fatal
+                return
+            card = next(iter(rec.values()), {}) if isinstance(rec, dict) else {}
+            for k_, v_ in card.items():
+                if "sclk" in k_.lower() and "speed" in k_.lower():
+                    digits = "".join(ch for ch in str(v_) if ch.isdigit())
+                    if digits:
+                        self.samples.append(int(digits))
+
+    def __enter__(self):
+        self._t = threading.Thread(target=self._poll, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._t.join(timeout=15)
 
 
 def cpu_baseline(inp, budget_s):
-    """Time the float64 oracle on a bounded sample of whole heads."""
+    """Time the float64 oracle (forward and backward separately) on whole
+    heads of the workload, with every core of this process's affinity set
+    as BLAS threads, for about budget_s seconds."""
     import numpy as np
     from threadpoolctl import threadpool_info, threadpool_limits
 
@@ -140,29 +172,36 @@ def cpu_baseline(inp, budget_s):
 
     q, k, v, do = (inp[n].float().numpy() for n in ("q", "k", "v", "do"))
     B, H, T, D = q.shape
-    cores = min(len(os.sched_getaffinity(0)), 16)
+    cores = len(os.sched_getaffinity(0))
     heads = [(b, h) for b in range(B) for h in range(H)]
-    done = 0
-    t0 = time.perf_counter()
+    done, t_fwd, t_bwd = 0, 0.0, 0.0
     with threadpool_limits(limits=cores):
         used = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-        while True:
+        while t_fwd + t_bwd < budget_s:
             b, h = heads[done % len(heads)]
+            t0 = time.perf_counter()
             A.forward_head(q[b, h], k[b, h], v[b, h], inp["scale"])
+            t1 = time.perf_counter()
             A.backward_head(q[b, h], k[b, h], v[b, h], do[b, h], inp["scale"])
+            t2 = time.perf_counter()
+            t_fwd += t1 - t0
+            t_bwd += t2 - t1
             done += 1
-            if time.perf_counter() - t0 >= budget_s:
-                break
-    dt = time.perf_counter() - t0
-    flops = 6 * done * D * T * (T + 1)
+    alg = 6 * done * D * T * (T + 1)
+    # dense products of the explicit T x T formulation: forward QK^T and PV,
+    # backward dV, dP, dQ, dK (12 T^2 D per head-problem)
     return {
-        "value": flops / dt / 1e12,
+        "value": alg / (t_fwd + t_bwd) / 1e12,
         "unit": "TFLOP/s",
         "cores": int(used),
         "kind": "oracle",
         "sample": "%d head-problems (cycling over the %d heads of B=%d, H=%d, T=%d, D=%d), "
-                  "float64 numpy oracle forward + backward, %.1f s, %s"
-                  % (done, B * H, B, H, T, D, dt, cpu_model()),
+                  "float64 numpy oracle, forward %.1f s + backward %.1f s, %d cores of %s"
+                  % (done, B * H, B, H, T, D, t_fwd, t_bwd, cores, cpu_model()),
+        "fwd_s_per_head": t_fwd / done,
+        "bwd_s_per_head": t_bwd / done,
+        "dense_fp64_gflops_fwd": 4 * T * T * D * done / t_fwd / 1e9,
+        "dense_fp64_gflops_bwd": 8 * T * T * D * done / t_bwd / 1e9,
     }
 
 
@@ -189,6 +228,141 @@ def time_steps(step, steps, warmup, stream):
     ev[1].record(stream)
     ev[1].synchronize()
     return ev[0].elapsed_time(ev[1]) / steps
+
+
+def gemm_rate(dev, n=8192, reps=20):
+    """Measured dense bf16 matrix-core rate of this machine (TFLOP/s): a large
+    square bf16 product through the vendor GEMM library, the attainable
+    counterpart of the spec peak."""
+    import torch
+
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    e1.synchronize()
+    return 2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12
+
+
+def gpu_inputs(B, H, T, D, dtype, dev, seed=0):
+    """Inputs of the workloads' recipe (projection of Gaussian activations,
+    or iid for float32), drawn with torch's generator on the GPU: the
+    `configs` timings need the shapes and value distribution, not the exact
+    numbers of the CPU generator the parity tests use."""
+    import torch
+
+    g = torch.Generator(device=dev).manual_seed(seed)
+    if dtype == "f32":
+        return [torch.randn(B, H, T, D, device=dev, generator=g) for _ in range(4)]
+    C = H * D
+    x = torch.randn(B * T, C, device=dev, generator=g)
+    out = []
+    for _ in range(3):
+        w = torch.randn(C, C, device=dev, generator=g) * 0.02
+        out.append((x @ w).view(B, T, H, D).transpose(1, 2).contiguous().bfloat16())
+    out.append((torch.randn(B, H, T, D, device=dev, generator=g) * 0.01).bfloat16())
+    return out
+
+
+class Step:
+    """One forward + backward of a dense [B,H,T,D] problem through the C ABI,
+    launch by launch (bf16 or float32 entry points)."""
+
+    def __init__(self, G, q, k, v, do, scale, stream):
+        import torch
+
+        self.lib = G.library()
+        self.G = G
+        B, H, T, D = q.shape
+        self.shape = (B, H, T, D)
+        f32 = q.dtype == torch.float32
+        self.q, self.k, self.v, self.do = q, k, v, do
+        self.o = torch.empty_like(q)
+        self.lse = torch.empty((B, H, T), dtype=torch.float32, device=q.device)
+        self.dq, self.dk, self.dv = (torch.empty_like(q) for _ in range(3))
+        self.wsb = G.workspace_bytes(B, H, T, D, f32)
+        self.ws = torch.empty(self.wsb, dtype=torch.uint8, device=q.device)
+        self.sc = scale
+        self.sp = stream.cuda_stream
+        sfx = "_f32" if f32 else ""
+        self.fn = [getattr(self.lib, "gptattn_fwd" + sfx),
+                   getattr(self.lib, "gptattn_bwd_dq" + sfx),
+                   getattr(self.lib, "gptattn_bwd_dkdv" + sfx)]
+
+    def launch(self, i):
+        B, H, T, D = self.shape
+        P = lambda t: t.data_ptr()  # noqa: E731
+        if i == 0:
+            rc = self.fn[0](P(self.q), P(self.k), P(self.v), P(self.o), P(self.lse), B, H, T, D,
+                            self.sc, self.sp)
+        elif i == 1:
+            rc = self.fn[1](P(self.q), P(self.k), P(self.v), P(self.o), P(self.do), P(self.lse),
+                            P(self.dq), B, H, T, D, self.sc, P(self.ws), self.wsb, self.sp)
+        else:
+            rc = self.fn[2](P(self.q), P(self.k), P(self.v), P(self.do), P(self.lse), P(self.dk),
+                            P(self.dv), B, H, T, D, self.sc, P(self.ws), self.wsb, self.sp)
+        if rc != 0:
+            raise RuntimeError("%s: %s" % (LAUNCHES[i], self.G.status_string(rc)))
+
+    def __call__(self):
+        for i in range(3):
+            self.launch(i)
+
+
+LAUNCHES = ("attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv")
+
+
+def per_kernel_pass(step, steps, stream, flush):
+    """Each kernel's average duration (ms) with an event at every launch
+    boundary, the caches flushed before each step (outside the events)."""
+    import torch
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    for e in ev:
+        if flush is not None:
+            flush.fill_(1)
+        for i in range(3):
+            e[i].record(stream)
+            step.launch(i)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    return [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / steps for i in range(3)]
+
+
+def workload_configs(G, dev, stream, steps, flush):
+    """The pages' other workloads, timed like the main one (cold caches,
+    events at every launch boundary)."""
+    from causal_self_attention_gptattn_amd import workloads as W
+
+    out = {}
+    for name, w in W.WORKLOADS.items():
+        q, k, v, do = gpu_inputs(w.B, w.H, w.T, w.D, w.dtype, dev)
+        st = Step(G, q, k, v, do, W.default_scale(w.D), stream)
+        for _ in range(3):
+            st()
+        ks = per_kernel_pass(st, steps, stream, flush)
+        ms = sum(ks)
+        flops = 6 * unit_flops(w.N, w.T, w.D)
+        table = kernel_table(w.N, w.T, w.D, 4 if w.dtype == "f32" else 2)
+        rec = {"B": w.B, "H": w.H, "T": w.T, "D": w.D, "dtype": w.dtype,
+               "ms_per_step": round(ms, 5), "alg_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+               "pct_of_bf16_mfma_peak": round(100.0 * flops / (ms * 1e-3) / 1e12
+                                              / PEAK_BF16_TFLOPS, 2),
+               "kernels_ms": {n: round(t, 5) for n, t in zip(LAUNCHES, ks)}}
+        dom = max(range(3), key=lambda i: ks[i])
+        rl = roofline(table[LAUNCHES[dom]]["flops"], table[LAUNCHES[dom]]["bytes"],
+                      ks[dom] * 1e-3)
+        rec["roofline"] = {"kernel": LAUNCHES[dom], "bound": rl["bound"],
+                           "frac": round(rl["frac"], 4)}
+        out[name] = rec
+        del st, q, k, v, do
+    return out
 
 
 def variants(G, inp, dev, stream, steps):
@@ -226,7 +400,7 @@ def variants(G, inp, dev, stream, steps):
         return step
 
     lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
-    ws = torch.empty(B * H * T * 4, dtype=torch.uint8, device=dev)
+    ws = torch.empty(2 * B * H * T * 4, dtype=torch.uint8, device=dev)
 
     # packed [B, T, 3C] projection output and packed gradient buffer
     x = torch.cat([t.transpose(1, 2).reshape(B, T, H * D) for t in (q0, k0, v0)], dim=-1)
@@ -279,13 +453,12 @@ def main():
     ap.add_argument("--workload", default="gpt2_124m")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
-    ap.add_argument("--cold-steps", type=int, default=20,
-                    help="extra steps timed with the caches flushed before each one")
+    ap.add_argument("--config-steps", type=int, default=10,
+                    help="timed steps per workload in the configs block (0 = skip it)")
     ap.add_argument("--variant-steps", type=int, default=20,
                     help="timed steps per strided-entry-point variant (0 = skip them)")
-    ap.add_argument("--smi-seconds", type=float, default=15.0,
-                    help="at most this long, run steps while rocm-smi reads sclk and power "
-                         "(0 = skip)")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="only the timed steps and the per-kernel pass (for profiling)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 5 device-to-device copies of MIB MiB (calibrates the "
                          "HBM byte counters against a copy of known size) and exit")
@@ -326,103 +499,71 @@ def main():
     inp = W.workload_inputs(w.name, seed=0)
     B, H, T, D, N = w.B, w.H, w.T, w.D, w.N
     sc = inp["scale"]
-    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
-    o = torch.empty_like(q)
-    lse = torch.empty((B, H, T), dtype=torch.float32, device=dev)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    ws_bytes = G.workspace_bytes(B, H, T, D)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    lib = G.library()
-    P = lambda t: t.data_ptr()  # noqa: E731
     stream = torch.cuda.current_stream(dev)
-    sp = stream.cuda_stream
-
-    def fwd():
-        return lib.gptattn_fwd(P(q), P(k), P(v), P(o), P(lse), B, H, T, D, sc, sp)
-
-    def bdq():
-        return lib.gptattn_bwd_dq(P(q), P(k), P(v), P(o), P(do), P(lse), P(dq), B, H, T, D, sc,
-                                  P(ws), ws_bytes, sp)
-
-    def bdkdv():
-        return lib.gptattn_bwd_dkdv(P(q), P(k), P(v), P(do), P(lse), P(dk), P(dv), B, H, T, D,
-                                    sc, P(ws), ws_bytes, sp)
-
-    launches = [("attn_fwd", fwd), ("attn_bwd_dq", bdq), ("attn_bwd_dkdv", bdkdv)]
-
-    def step(events=None, around=None):
-        """One step.  events: one event per launch boundary (len(launches) + 1),
-        or with `around` = i a pair recorded just before and after launch i."""
-        for i, (name, fn) in enumerate(launches):
-            if events is not None and (around is None or around == i):
-                events[0 if around is not None else i].record(stream)
-            rc = fn()
-            if rc != 0:
-                raise RuntimeError("%s: %s" % (name, G.status_string(rc)))
-            if events is not None and around == i:
-                events[1].record(stream)
-        if events is not None and around is None:
-            events[len(launches)].record(stream)
+    q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
+    step = Step(G, q, k, v, do, sc, stream)
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device=dev)
+    table = kernel_table(N, T, D)
+    flops = 6 * unit_flops(N, T, D)
 
     print("bench: warmup %d steps" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
 
-    # per-kernel durations: a pass with an event at every launch boundary
+    # per-kernel table: events at every launch boundary, caches flushed
     print("bench: per-kernel pass %d steps" % args.steps, file=sys.stderr, flush=True)
-    pev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)]
-           for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(pev[i])
-    torch.cuda.synchronize(dev)
-    per_kernel_ms = {name: 0.0 for name, _ in launches}
-    for e in pev:
-        for i, (name, _) in enumerate(launches):
-            per_kernel_ms[name] += e[i].elapsed_time(e[i + 1])
-    per_kernel_ms = {k_: t / args.steps for k_, t in per_kernel_ms.items()}
-    dom = max(per_kernel_ms, key=per_kernel_ms.get)
-    dom_i = [name for name, _ in launches].index(dom)
+    pk = per_kernel_pass(step, args.steps, stream, flush)
+    dom_i = max(range(3), key=lambda i: pk[i])
+    dom = LAUNCHES[dom_i]
 
-    # timed steps: two events per step, around the dominant kernel
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    # timed steps: caches flushed before each (outside the events); events
+    # before the forward, before the dominant kernel and after the step
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
-    torch.cuda.synchronize(dev)
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(evs[i], around=dom_i)
-    torch.cuda.synchronize(dev)
-    wall = time.perf_counter() - t0
-
-    dom_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
-    step_ms = [evs[i - 1][1].elapsed_time(evs[i][1]) for i in range(1, args.steps)]
-    q1, med, q3 = (float(x) for x in np.percentile(step_ms, [25, 50, 75]))
-
-    # Cold-cache steps: overwrite a 1 GiB buffer before each (outside events).
-    cold_ms = None
-    if args.cold_steps > 0:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
-               for _ in range(args.cold_steps)]
-        for e in cev:
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    with ClockSampler() as clocks:
+        torch.cuda.synchronize(dev)
+        t0 = time.perf_counter()
+        for e in evs:
             flush.fill_(1)
             e[0].record(stream)
-            step()
-            e[1].record(stream)
+            for i in range(3):
+                if i == dom_i:
+                    e[1].record(stream)
+                step.launch(i)
+            e[2].record(stream)
         torch.cuda.synchronize(dev)
-        cold_ms = sum(a.elapsed_time(b) for a, b in cev) / args.cold_steps
-        del flush
+        wall = time.perf_counter() - t0
+        # keep the GPU at this load until rocm-smi has answered at least once
+        t1 = time.perf_counter()
+        while not clocks.samples and time.perf_counter() - t1 < 5.0:
+            for _ in range(10):
+                flush.fill_(1)
+                step()
+            torch.cuda.synchronize(dev)
+    step_ms = np.array([a.elapsed_time(c) for a, _, c in evs])
+    dom_ms = float(np.mean([b.elapsed_time(c) if dom_i == 2 else 0.0 for _, b, c in evs]))
+    if dom_i != 2:  # the dominant kernel is followed by others: use the per-kernel pass
+        dom_ms = pk[dom_i]
+    ms = float(step_ms.mean())
+    value = flops / (ms * 1e-3) / 1e12
+    q1, med, q3 = (float(x) for x in np.percentile(step_ms, [25, 50, 75]))
 
-    flops = 6 * N * D * T * (T + 1)
-    ms = wall * 1e3 / args.steps
-    value = flops / (wall / args.steps) / 1e12
-    table = kernel_table(N, T, D)
-    achieved = table[dom]["flops"] / (dom_ms * 1e-3) / 1e12
+    # warm steps: back to back, no flush, wall clock
+    torch.cuda.synchronize(dev)
+    tw = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize(dev)
+    warm_ms = (time.perf_counter() - tw) * 1e3 / args.steps
+
+    rl = roofline(table[dom]["flops"], table[dom]["bytes"], dom_ms * 1e-3)
     kernels = {}
-    for name, t_ms in per_kernel_ms.items():
+    for name, t_ms in zip(LAUNCHES, pk):
         tf = table[name]["flops"] / (t_ms * 1e-3) / 1e12
         gbs = table[name]["bytes"] / (t_ms * 1e-3) / 1e9
         eps = table[name]["exps"] / (t_ms * 1e-3)
+        r = roofline(table[name]["flops"], table[name]["bytes"], t_ms * 1e-3)
         kernels[name] = {
             "ms": round(t_ms, 5),
             "alg_tflops": round(tf, 2),
@@ -431,28 +572,30 @@ def main():
             "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
             "exp_frac": round(eps / PEAK_EXP_PER_S, 4),
+            "bound": r["bound"],
+            "frac": round(r["frac"], 4),
         }
-    traffic = measured_traffic(dom)
 
-    # clocks and power while the step runs (outside every timed region)
-    def some_steps():
-        for _ in range(20):
-            step()
-        torch.cuda.synchronize(dev)
-
-    gpu_state = clocks_under_load(some_steps, args.smi_seconds) if args.smi_seconds > 0 else None
-
+    extras = not args.no_extras
+    gemm = None
+    if extras:
+        print("bench: dense bf16 GEMM rate", file=sys.stderr, flush=True)
+        gemm = gemm_rate(dev)
+    cfgs = None
+    if extras and args.config_steps > 0:
+        print("bench: the other workloads", file=sys.stderr, flush=True)
+        cfgs = workload_configs(G, dev, stream, args.config_steps, flush)
     var = None
-    if args.variant_steps > 0:
+    if extras and args.variant_steps > 0:
         print("bench: strided entry points", file=sys.stderr, flush=True)
         var = variants(G, inp, dev, stream, args.variant_steps)
-
     base = None
-    if args.cpu_budget > 0:
+    if extras and args.cpu_budget > 0:
         print("bench: oracle CPU baseline (%.0f s budget)" % args.cpu_budget,
               file=sys.stderr, flush=True)
         base = cpu_baseline(inp, args.cpu_budget)
 
+    sclk = clocks.samples
     out = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -467,27 +610,35 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "B": B, "H": H, "T": T, "D": D, "causal": True,
-                   "scale": sc, "alg_gflop_per_step": round(flops / 1e9, 3)},
+                   "scale": sc, "alg_gflop_per_step": round(flops / 1e9, 3),
+                   "caches": "flushed before every timed step"},
         "pct_of_bf16_mfma_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "measured_bf16_gemm_tflops": None if gemm is None else round(gemm, 1),
+        "pct_of_measured_gemm_rate": None if gemm is None else round(100.0 * value / gemm, 2),
+        "warm": {"ms_per_step": round(warm_ms, 5),
+                 "tflops": round(flops / (warm_ms * 1e-3) / 1e12, 2)},
         # the FlashAttention-paper convention (7 D T^2 per head-problem, counts
         # the backward's recomputation); labelled, never mixed with `value`
-        "fa_convention_tflops": round(7 * N * D * T * T / (wall / args.steps) / 1e12, 2),
-        "step_ms_events": {"median": round(med, 5), "min": round(float(min(step_ms)), 5),
+        "fa_convention_tflops": round(7 * N * D * T * T / (ms * 1e-3) / 1e12, 2),
+        "step_ms_events": {"median": round(med, 5), "min": round(float(step_ms.min()), 5),
                            "iqr": round(q3 - q1, 5)},
+        "timed_region_wall_s": round(wall, 4),
         "kernels": kernels,
-        "cold_cache_ms_per_step": None if cold_ms is None else round(cold_ms, 5),
         "roofline": {
             "kernel": dom,
             "kernel_ms": round(dom_ms, 5),
-            "bound": "mfma",
-            "achieved": round(achieved, 2),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-            "traffic": traffic,
+            "bound": rl["bound"],
+            "achieved": round(rl["achieved"], 2),
+            "peak": rl["peak"],
+            "unit": rl["unit"],
+            "frac": round(rl["frac"], 4),
+            "traffic": measured_traffic(dom),
         },
         "cpu_baseline": base,
-        "gpu_under_load": gpu_state,
+        "sclk_mhz_under_load": {"samples": len(sclk),
+                                "median": int(np.median(sclk)) if sclk else None,
+                                "min": min(sclk) if sclk else None},
+        "configs": cfgs,
         "variants": var,
     }
     print(json.dumps(out), flush=True)

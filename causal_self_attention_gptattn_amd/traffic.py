@@ -34,9 +34,10 @@ def _per_kernel_kib(path, counter):
         for row in csv.DictReader(f):
             if row["Counter_Name"] != counter:
                 continue
-            # the launch a kernel serves: attn_bwd_dq16<...> and
-            # attn_bwd_dkdv16w<...> (16-row waves) count as attn_bwd_dq / _dkdv
-            m = re.search(r"::(attn_[a-z_]+?)(?:16w?)?<", row["Kernel_Name"]) or re.search(
+            # the launch a kernel serves: attn_bwd_dq16<...>, attn_bwd_dkdv16w<...>
+            # (16-row waves) and the head-size-64 kernels (attn_bwd_dkdv64<...>,
+            # ...) count as attn_bwd_dq / attn_bwd_dkdv / attn_fwd
+            m = re.search(r"::(attn_[a-z_]+?)(?:16w?|64)?<", row["Kernel_Name"]) or re.search(
                 r"(__amd_rocclr_copyBuffer)", row["Kernel_Name"])
             if not m:
                 continue

@@ -77,6 +77,7 @@ def test_traffic_counters_are_keyed_by_launch(tmp_path):
             ("void gptattn::(anonymous namespace)::attn_bwd_dq<128, true>(...)", 40.0),
             ("void gptattn::(anonymous namespace)::attn_bwd_dkdv<64, 64>(...)", 30.0),
             ("void gptattn::(anonymous namespace)::attn_bwd_dkdv16w<128, false>(...)", 50.0),
+            ("void gptattn::(anonymous namespace)::attn_bwd_dkdv64<4>(...)", 60.0),
             ("__amd_rocclr_copyBuffer", 7.0)]
     path = tmp_path / "c.csv"
     with open(path, "w") as f:
@@ -84,5 +85,32 @@ def test_traffic_counters_are_keyed_by_launch(tmp_path):
         for name, v in rows:
             f.write('"%s",FETCH_SIZE,%g\n' % (name, v))
     got = traffic._per_kernel_kib(str(path), "FETCH_SIZE")
-    assert got == {"attn_fwd": 10.0, "attn_bwd_dq": 30.0, "attn_bwd_dkdv": 40.0,
+    assert got == {"attn_fwd": 10.0, "attn_bwd_dq": 30.0, "attn_bwd_dkdv": (30.0 + 50.0 + 60.0) / 3,
                    "__amd_rocclr_copyBuffer": 7.0}
+
+
+def test_roofline_takes_the_tighter_roof(bench):
+    """frac = max(F / peak_flops, B / peak_bw) / t, reported against the roof
+    that term belongs to."""
+    # the GPT-2 dK/dV launch: 29.0 GFLOP, 114.4 MB -> the HBM term is larger
+    N, T, D = 144, 1024, 64
+    k = bench.kernel_table(N, T, D)["attn_bwd_dkdv"]
+    t = 50e-6
+    r = bench.roofline(k["flops"], k["bytes"], t)
+    f_term = k["flops"] / (bench.PEAK_BF16_TFLOPS * 1e12)
+    b_term = k["bytes"] / (bench.PEAK_HBM_GBS * 1e9)
+    assert b_term > f_term
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == bench.PEAK_HBM_GBS
+    assert abs(r["frac"] - max(f_term, b_term) / t) < 1e-12
+    assert abs(r["achieved"] - k["bytes"] / t / 1e9) < 1e-6
+    # the GPT-3-shaped layer's dK/dV launch is matrix-bound
+    k = bench.kernel_table(96, 2048, 128)["attn_bwd_dkdv"]
+    r = bench.roofline(k["flops"], k["bytes"], 300e-6)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s"
+    assert abs(r["frac"] - k["flops"] / (bench.PEAK_BF16_TFLOPS * 1e12) / 300e-6) < 1e-12
+
+
+def test_float32_tensor_bytes(bench):
+    t16 = bench.kernel_table(4, 64, 16)["attn_fwd"]["bytes"]
+    t32 = bench.kernel_table(4, 64, 16, 4)["attn_fwd"]["bytes"]
+    assert t32 - t16 == 4 * (4 * 64 * 16 * 2)
