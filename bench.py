@@ -18,12 +18,14 @@ stream (before the forward, before the dominant kernel, after the step):
 the step time, and the dominant kernel's time for the roofline, both
 measured live over the timed steps.  The warm figure (steps back to back,
 no flush, wall clock) is reported beside it.  A separate pass with an event
-at every launch boundary gives the per-kernel table.
+at every launch boundary gives the per-kernel table.  The clock (sclk) is
+sampled with rocm-smi while the same flushed steps keep running right after
+the timed region.
 
 Prints one JSON line with, besides the contract's keys: the roofline of the
 dominant kernel against whichever of its two roofs (bf16 MFMA, HBM) is the
 tighter one, the measured dense bf16 GEMM rate of the box (the attainable
-matrix-core peak), sclk samples taken while the timed steps run, the CPU
+matrix-core peak), sclk samples taken under the same load, the CPU
 oracle baseline, the other workloads of the pages (`configs`), and the
 strided entry points (`variants`).
 """
@@ -131,8 +133,9 @@ class ClockSampler:
     """Polls rocm-smi for sclk (and power) in a background thread while the
     GPU works; best effort (no samples when the tool is missing)."""
 
-    def __init__(self):
+    def __init__(self, enabled=True):
         self.samples = []
+        self.enabled = enabled
         self._stop = threading.Event()
         self._t = None
 
@@ -152,13 +155,15 @@ class ClockSampler:
                         self.samples.append(int(digits))
 
     def __enter__(self):
-        self._t = threading.Thread(target=self._poll, daemon=True)
-        self._t.start()
+        if self.enabled:
+            self._t = threading.Thread(target=self._poll, daemon=True)
+            self._t.start()
         return self
 
     def __exit__(self, *exc):
         self._stop.set()
-        self._t.join(timeout=15)
+        if self._t is not None:
+            self._t.join(timeout=15)
 
 
 def cpu_baseline(inp, budget_s):
@@ -457,6 +462,8 @@ def main():
                     help="timed steps per workload in the configs block (0 = skip it)")
     ap.add_argument("--variant-steps", type=int, default=20,
                     help="timed steps per strided-entry-point variant (0 = skip them)")
+    ap.add_argument("--no-smi", action="store_true",
+                    help="do not poll rocm-smi for clocks while the timed steps run")
     ap.add_argument("--no-extras", action="store_true",
                     help="only the timed steps and the per-kernel pass (for profiling)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -521,22 +528,25 @@ def main():
     # before the forward, before the dominant kernel and after the step
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    with ClockSampler() as clocks:
-        torch.cuda.synchronize(dev)
-        t0 = time.perf_counter()
-        for e in evs:
-            flush.fill_(1)
-            e[0].record(stream)
-            for i in range(3):
-                if i == dom_i:
-                    e[1].record(stream)
-                step.launch(i)
-            e[2].record(stream)
-        torch.cuda.synchronize(dev)
-        wall = time.perf_counter() - t0
-        # keep the GPU at this load until rocm-smi has answered at least once
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for e in evs:
+        flush.fill_(1)
+        e[0].record(stream)
+        for i in range(3):
+            if i == dom_i:
+                e[1].record(stream)
+            step.launch(i)
+        e[2].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - t0
+    # The clock under this load: rocm-smi polled while the same flushed steps
+    # keep running right after the timed region (a rocm-smi call during the
+    # timed steps stalls the step it lands on by half a millisecond, so it
+    # stays out of them).
+    with ClockSampler(not args.no_smi) as clocks:
         t1 = time.perf_counter()
-        while not clocks.samples and time.perf_counter() - t1 < 5.0:
+        while clocks.enabled and len(clocks.samples) < 3 and time.perf_counter() - t1 < 5.0:
             for _ in range(10):
                 flush.fill_(1)
                 step()
@@ -621,7 +631,8 @@ def main():
         # the backward's recomputation); labelled, never mixed with `value`
         "fa_convention_tflops": round(7 * N * D * T * T / (ms * 1e-3) / 1e12, 2),
         "step_ms_events": {"median": round(med, 5), "min": round(float(step_ms.min()), 5),
-                           "iqr": round(q3 - q1, 5)},
+                           "max": round(float(step_ms.max()), 5), "iqr": round(q3 - q1, 5),
+                           "all": [round(float(x), 4) for x in step_ms]},
         "timed_region_wall_s": round(wall, 4),
         "kernels": kernels,
         "roofline": {
