@@ -51,7 +51,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # wave64 instruction per 8 cycles per SIMD), i.e. 256 CU x 4 SIMD x 64 lanes
 # / 8 cycles x 2.4 GHz exponentials per second.
 PEAK_EXP_PER_S = 256 * 4 * 64 / 8 * 2.4e9
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gpt2_124m.json")
+TRAFFIC_DIR = os.path.join(ROOT, "profiles")  # traffic_<workload>.json
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_d64.hip", "attn_common.h"]
 FLUSH_BYTES = 1 << 30
 
@@ -71,9 +71,11 @@ def kernel_table(N, T, D, elem=2):
     return {
         # QK^T and PV; reads Q, K, V, writes O and lse
         "attn_fwd": {"flops": 2 * u, "bytes": 4 * t + r, "exps": x},
-        # the dQ product; reads Q, K, V, O, dO, lse, writes dQ and the row term
-        "attn_bwd_dq": {"flops": 1 * u, "bytes": 6 * t + 2 * r, "exps": x},
-        # dP, dV and dK products; reads Q, K, V, dO, lse, row term, writes dK, dV
+        # the dQ product; reads Q, K, V, O, dO, lse, writes dQ and two row
+        # vectors (the softmax row term, lse / scale) for the dK/dV kernel
+        "attn_bwd_dq": {"flops": 1 * u, "bytes": 6 * t + 3 * r, "exps": x},
+        # dP, dV and dK products; reads Q, K, V, dO and the two row vectors,
+        # writes dK, dV
         "attn_bwd_dkdv": {"flops": 3 * u, "bytes": 6 * t + 2 * r, "exps": x},
     }
 
@@ -101,11 +103,12 @@ def source_sha():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch from the committed counter profile, or None if
-    there is none or the kernel sources changed since it was taken."""
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed counter profile of this
+    workload, or None if there is none or the kernel sources changed since it
+    was taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(os.path.join(TRAFFIC_DIR, "traffic_%s.json" % workload)) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -643,7 +646,7 @@ def main():
             "peak": rl["peak"],
             "unit": rl["unit"],
             "frac": round(rl["frac"], 4),
-            "traffic": measured_traffic(dom),
+            "traffic": measured_traffic(dom, w.name),
         },
         "cpu_baseline": base,
         "sclk_mhz_under_load": {"samples": len(sclk),

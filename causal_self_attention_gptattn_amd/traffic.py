@@ -10,7 +10,7 @@ Usage (from the repository root, after the four counter runs)::
     python -m causal_self_attention_gptattn_amd.traffic \\
         --fetch DIR/bench_counter_collection.csv --write DIR/bench_counter_collection.csv \\
         --copy-fetch DIR/copy_counter_collection.csv --copy-write DIR/copy_counter_collection.csv \\
-        --copy-mib 256 --out profiles/traffic_gpt2_124m.json
+        --copy-mib 256 --workload gpt2_124m --out profiles/traffic_gpt2_124m.json
 """
 
 import argparse
@@ -45,6 +45,13 @@ def _per_kernel_kib(path, counter):
     return {k: sum(v) / len(v) for k, v in vals.items()}
 
 
+def _describe(name):
+    from causal_self_attention_gptattn_amd import workloads as W
+
+    w = W.WORKLOADS[name]
+    return "%s (B=%d, H=%d, T=%d, D=%d, %s)" % (w.name, w.B, w.H, w.T, w.D, w.dtype)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--fetch", required=True)
@@ -53,6 +60,7 @@ def main():
     ap.add_argument("--copy-write", required=True)
     ap.add_argument("--copy-mib", type=int, required=True)
     ap.add_argument("--out", required=True)
+    ap.add_argument("--workload", default="gpt2_124m")
     ap.add_argument("--command", default="")
     args = ap.parse_args()
 
@@ -65,7 +73,7 @@ def main():
     fetch = _per_kernel_kib(args.fetch, "FETCH_SIZE")
     write = _per_kernel_kib(args.write, "WRITE_SIZE")
     rec = {
-        "workload": "gpt2_124m (B=12, H=12, T=1024, D=64, bf16)",
+        "workload": _describe(args.workload),
         "source_sha": bench.source_sha(),
         "calibration": {"copy_bytes": copy_bytes, "fetch_scale": round(f_scale, 4),
                         "write_scale": round(w_scale, 4)},

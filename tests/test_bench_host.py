@@ -33,7 +33,7 @@ def test_work_counts_at_the_gpt2_shape(bench):
     # one bf16 tensor 18.87 MB, one float32 row vector N*T*4 bytes
     t, r = N * T * D * 2, N * T * 4
     assert tab["attn_fwd"]["bytes"] == 4 * t + r
-    assert tab["attn_bwd_dq"]["bytes"] == 6 * t + 2 * r
+    assert tab["attn_bwd_dq"]["bytes"] == 6 * t + 3 * r
     assert tab["attn_bwd_dkdv"]["bytes"] == 6 * t + 2 * r
     assert all(k["exps"] == N * T * (T + 1) // 2 for k in tab.values())
 
@@ -50,14 +50,16 @@ def test_traffic_is_reported_only_for_the_sources_it_was_taken_with(bench, tmp_p
                                                                   monkeypatch):
     rec = {"source_sha": bench.source_sha(),
            "kernels": {"attn_bwd_dkdv": {"fetch_bytes": 100, "write_bytes": 23}}}
-    path = tmp_path / "traffic.json"
+    path = tmp_path / "traffic_gpt2_124m.json"
     path.write_text(json.dumps(rec))
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(path))
-    assert bench.measured_traffic("attn_bwd_dkdv") == 123
-    assert bench.measured_traffic("attn_fwd") is None
+    monkeypatch.setattr(bench, "TRAFFIC_DIR", str(tmp_path))
+    assert bench.measured_traffic("attn_bwd_dkdv", "gpt2_124m") == 123
+    assert bench.measured_traffic("attn_fwd", "gpt2_124m") is None
+    # another workload's counters are never reported
+    assert bench.measured_traffic("attn_bwd_dkdv", "gpt3_2048") is None
     rec["source_sha"] = "0" * 16
     path.write_text(json.dumps(rec))
-    assert bench.measured_traffic("attn_bwd_dkdv") is None
+    assert bench.measured_traffic("attn_bwd_dkdv", "gpt2_124m") is None
 
 
 def test_more_than_one_gpu_is_refused():
