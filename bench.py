@@ -12,7 +12,8 @@ implementation work and is not counted.
 
 Timing.  `value` is the cold-cache figure: before every timed step a 1 GiB
 buffer is overwritten (outside the HIP events), which evicts the step's
-227.7 MB working set from the 256 MB last-level cache, so every step reads
+152.8 MB working set (Q, K, V, O, dO, dQ, dK, dV, lse and the two
+workspace vectors) from the 256 MB last-level cache, so every step reads
 its inputs from HBM.  Each timed step carries three events on the launch
 stream (before the forward, before the dominant kernel, after the step):
 the step time, and the dominant kernel's time for the roofline, both
@@ -35,6 +36,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import subprocess
 import sys
 import threading
@@ -95,11 +97,21 @@ def roofline(flops, nbytes, seconds):
             "frac": ach / PEAK_BF16_TFLOPS}
 
 
+def code_of(text):
+    """A kernel source with its comments and blank space taken out: what the
+    compiler sees (the sources hold no string literal with // or /*)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_sha():
+    """Hash of the kernel code (comments excluded) that counter profiles
+    are tied to."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "causal_self_attention_gptattn_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "causal_self_attention_gptattn_amd", "csrc", name)) as f:
+            h.update(code_of(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,31 +1,29 @@
-// Causal attention at head size 64 without dropout: software-pipelined
-// kernels for gfx950 (bf16 storage, float32 accumulation).
+// dK / dV of causal attention at head size 64 without dropout, for gfx950
+// (bf16 storage, float32 accumulation).
 //
 // The operation is the one attn_bf16.hip computes (lecture description
 // "Let's build GPT: from scratch, in code, spelled out", chapters "version 3:
 // adding softmax" and "version 4: self-attention"; the chain rule of the
-// softmax for the backward pass).  These kernels serve the most common head
-// size of the pages' models (GPT-2 124M / XL, the character model: 64) and
-// are organised around what bounds them on this chip:
+// softmax for the backward pass).  This kernel serves the most common head
+// size of the pages' models (GPT-2 124M / XL: 64) on sequences longer than
+// 256 keys, and is organised around what bounds it on this chip:
 //
-//  * Every wave owns 32 rows (keys in dK/dV) and runs all products on
+//  * Every wave owns 32 keys and runs all four products on
 //    v_mfma_f32_32x32x16_bf16: each 1 KiB operand read from LDS feeds 32
 //    cycles of matrix work, half the LDS bytes per product of the 16 x 16 x 32
-//    product, so LDS bandwidth stays below the matrix-core rate.
-//  * A staged 64-row tile is taken as two 32-row halves, and the work of a
-//    tile is issued in four phases so that the matrix cores and the vector
-//    units overlap inside one wave: the products of half 1 run while the
-//    vector units turn half 0's scores into weights, and half 0's weighted
-//    products run while half 1's weights are formed.  One workgroup barrier
-//    per tile; the copy of the next tile (HBM -> LDS, no registers) is issued
-//    right after it, so it has a whole tile of time to land.
+//    product, and 128 keys per workgroup halve the Q/dO tile copies per key
+//    against 64.
+//  * Q/dO tiles go HBM -> LDS (no registers) through a ring of three
+//    buffers: the copy of tile t + 2 is issued as tile t starts, and a wave
+//    waits only for the copies older than the newest one, so each copy has
+//    two tiles of time to land.  One workgroup barrier per tile.
 //  * Row statistics enter the products as accumulator seeds instead of
-//    vector work: the dK/dV kernel starts S at -lse/scale and dP at -delta,
-//    so P = exp2(S * scale * log2 e) and dS = P * dP.
-//
-// Tiles that straddle the edge of visibility (the diagonal, a band edge, the
-// end of the sequence) take a plain masked path; only interior tiles take the
-// pipelined one.
+//    vector work: S starts at -lse/scale and dP at -delta (both stored by the
+//    dQ kernel, copied in with the tile), so P = exp2(S * scale * log2 e) and
+//    dS = P * dP.
+//  * Every tile runs the same products; a tile that straddles the edge of
+//    visibility differs only in how its weights are formed (masked element
+//    by element), so the accumulators never leave their registers.
 #include "attn_common.h"
 #include "launch.h"
 

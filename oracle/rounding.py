@@ -7,8 +7,12 @@ same points -- P rounded to bf16 before it weights V and dO, dS rounded to
 bf16 before the dQ and dK products, outputs rounded once to bf16 -- so that
 its distance from the float64 definition estimates the error floor that bf16
 storage alone imposes.  It is reported beside the GPU error and is not a
-gate.  Rounding uses PyTorch's CPU float -> bfloat16 conversion (round to
-nearest even).
+gate.  Rounding uses PyTorch's CPU conversion, which takes a float64
+value to float32 and then to bfloat16, each to nearest with ties to even:
+the kernels round float32 values.  Pinned by tests/test_oracle_rounding.py
+(an independent rounding written from the format, a scalar-loop twin that
+must match bit for bit and fails with any one rounding left out, and a
+hand-worked case).
 """
 
 import numpy as np

@@ -62,6 +62,14 @@ def test_traffic_is_reported_only_for_the_sources_it_was_taken_with(bench, tmp_p
     assert bench.measured_traffic("attn_bwd_dkdv", "gpt2_124m") is None
 
 
+def test_source_hash_ignores_comments_only(bench):
+    """Counter profiles stay valid across comment edits, not code edits."""
+    a = "int f(int x) {  // twice\n  return 2 * x; /* doubled */ }\n"
+    b = "/* header */\nint f(int x) {\n  return 2 * x;\n}\n"
+    c = "int f(int x) { return 3 * x; }"
+    assert bench.code_of(a) == bench.code_of(b) != bench.code_of(c)
+
+
 def test_more_than_one_gpu_is_refused():
     out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                          capture_output=True, text=True, timeout=120)
