@@ -304,7 +304,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv64(
   // Tile qt from buffer cur; the copy of tile qt + 2 goes into buffer nxt
   // (free: its tile qt - 1 was finished before the last barrier).  Before the
   // barrier, wait for the copy of tile qt + 1.
-  auto step = [&](int qt, const uint16_t* cur, uint16_t* nxt) {
+  auto step = [&](int qt, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
     const bool two = qt + 2 <= qt1;
     if (two) load_tile(qt + 2, nxt);
     const int q0 = qt * QT;
@@ -336,7 +336,264 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv64(
                 pb.Tk - k0w, lane);
 }
 
+
+// store_rows (attn_common.h) for a staging area that only the calling wave
+// uses: the LDS accesses of one wave are carried out in program order, so a
+// fence at wavefront scope (it keeps the compiler from moving LDS accesses
+// across it) replaces the workgroup barriers, and the waves of a workgroup
+// store their rows independently.
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ void store_rows_wave(uint16_t* lds, const f32x16* acc, float mul,
+                                                uint16_t* out, int rows_valid, int lane) {
+  constexpr int D = kD, RS = D + 8, DE = D / 32, CPR = D / 8, PASS = 16 * CPR / 64;
+  const int c = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if ((c >> 4) == half) {
+#pragma unroll
+      for (int e = 0; e < DE; ++e)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const u32x2 pk = {pack_bf16x2(acc[e][4 * u] * mul, acc[e][4 * u + 1] * mul),
+                            pack_bf16x2(acc[e][4 * u + 2] * mul, acc[e][4 * u + 3] * mul)};
+          *reinterpret_cast<u32x2*>(lds + (c & 15) * RS + 32 * e + 8 * u + 4 * g) = pk;
+        }
+    }
+    wave_lds_order();
+#pragma unroll
+    for (int p = 0; p < PASS; ++p) {
+      const int ch = lane + 64 * p, r = ch / CPR, cc = ch % CPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + r * RS + 8 * cc);
+      const int row = 16 * half + r;
+      if (row < rows_valid) *reinterpret_cast<u32x4*>(out + (long long)row * D + 8 * cc) = v;
+    }
+    wave_lds_order();
+  }
+}
+
+// The same kernel as a persistent grid, for dense tensors ([B][H][T][64],
+// rows contiguous): one workgroup per slot (two per CU), each walking a list
+// of (head, 128-key block) items.  The tile copies form one stream across
+// the items of a workgroup, so the three-buffer ring runs on from one item
+// into the next: the next item's first tiles are copied while the current
+// item's last tiles are computed, and the per-item start-up latency of a
+// one-shot workgroup is hidden.
+//
+// Item order: items sorted longest walk first (key block 0 of every head,
+// then key block 1, ...).  With X = 8 groups (heads n with n mod 8 = x;
+// workgroup g runs on XCD g mod 8, so a head's items stay on one XCD and its
+// tiles in one L2) and R workgroups per group, the workgroup with rank r in
+// its group takes the group's items r, 2R - 1 - r, 2R + r, 4R - 1 - r, ...:
+// a long item is paired with a short one, which balances the walks.
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv64p(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+    const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
+    const float* __restrict__ Seeds, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
+    Problem pb, int items, int R, int X) {
+  constexpr int D = kD, QT = kQT, NT = 64 * NW, KB = 32 * NW;
+  constexpr int BUF = 2 * QT * D + 4 * QT;
+  constexpr int LD = D + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t B0[BUF], B1[BUF], B2[BUF];
+  __shared__ __attribute__((aligned(16))) uint16_t Stg[NW * 16 * LD];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c = lane & 31, g = lane >> 5;
+  const int x = blockIdx.x % X, r = blockIdx.x / X;
+  const int NX = pb.N / X, M = items / X;  // heads and items per group
+
+  // k-th item of this workgroup: head n, first key k0 (-1 past the end),
+  // query tiles qt0..qt1
+  struct Item {
+    int n, k0, qt0, qt1;
+  };
+  auto item_at = [&](int k) {
+    Item it;
+    const int m = (k & 1) ? (k + 1) * R - 1 - r : k * R + r;
+    if (m >= M) {
+      it.n = 0;
+      it.k0 = -1;
+      it.qt0 = 0;
+      it.qt1 = -1;
+      return it;
+    }
+    const int kb = m / NX;
+    it.n = X * (m - kb * NX) + x;
+    it.k0 = kb * KB;
+    const int qlo = queries_lo(it.k0, pb), qhi = queries_hi(min(it.k0 + KB, pb.Tk) - 1, pb);
+    it.qt0 = qlo / QT;
+    it.qt1 = qhi >= qlo ? qhi / QT : it.qt0 - 1;
+    return it;
+  };
+
+  DkdvLane sw;
+  {
+    const int trr = tr_rowoff(lane), trc = tr_coloff(lane);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sw.fo[s] = swz<D>(c, 16 * s + 8 * g);
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      sw.tlo[e] = swz<D>(trr, 32 * e + trc);
+      sw.thi[e] = swz<D>(trr + 8, 32 * e + trc);
+    }
+  }
+
+  TileDMA<QT, D, NT> qs;
+  qs.init(tid, D);
+  const long long NTq = (long long)pb.N * pb.Tq;
+  // copy of tile qt of head n into buffer b (as in attn_bwd_dkdv64)
+  auto load_tile = [&](int n, int qt, uint16_t* b) {
+    const int q1 = qt * QT, valid = pb.Tq - q1;
+    const long long row = (long long)n * pb.Tq + q1;
+    qs.load(Q + row * D, valid, b);
+    qs.load(dO + row * D, valid, b + QT * D);
+    if (w == 0 && lane < 16) {
+      const int cnt = valid <= 0 ? 0 : valid < QT ? valid : QT;
+      const __amdgpu_buffer_rsrc_t re = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(Seeds + row), 0, __builtin_amdgcn_readfirstlane(cnt * 4),
+          kBufferWord3);
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(Seeds + NTq + row), 0, __builtin_amdgcn_readfirstlane(cnt * 4),
+          kBufferWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void*)(b + 2 * QT * D), 16, lane * 16, 0,
+                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void*)(b + 2 * QT * D + 2 * QT), 16,
+                                               lane * 16, 0, 0, 0);
+    }
+  };
+  constexpr int kDmaW = 2 * (QT * D / 8 / NT);
+  static_assert(kDmaW + 2 < 16, "vmcnt field");
+  auto wait_all_but_one = [&]() {
+    if (w == 0)
+      wait_vm_upto<kDmaW + 2>();
+    else
+      wait_vm_upto<kDmaW>();
+  };
+  auto es_of = [](const uint16_t* b) { return reinterpret_cast<const float*>(b + 2 * QT * D); };
+  auto ls_of = [](const uint16_t* b) {
+    return reinterpret_cast<const float*>(b + 2 * QT * D) + QT;
+  };
+
+  // K and V rows of an item's 32 keys for this wave: B operands of S and dP
+  auto load_kv = [&](const Item& it, bf16x8* kf, bf16x8* vf) {
+    const int k0w = it.k0 + 32 * w;
+    const long long row = (long long)it.n * pb.Tk + k0w;
+    RowBlock kr, vr;
+    kr.init(K + row * D, pb.Tk - k0w, D, c);
+    vr.init(V + row * D, pb.Tk - k0w, D, c);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      kf[s] = __builtin_bit_cast(bf16x8, kr.load(16 * s + 8 * g));
+      vf[s] = __builtin_bit_cast(bf16x8, vr.load(16 * s + 8 * g));
+    }
+  };
+  uint16_t* stage = Stg + w * 16 * LD;
+  auto store_item = [&](const Item& it, const f32x16* dkt, const f32x16* dvt) {
+    const int k0w = it.k0 + 32 * w;
+    const long long row = (long long)it.n * pb.Tk + k0w;
+    store_rows_wave(stage, dkt, pb.scale, dK + row * D, pb.Tk - k0w, lane);
+    store_rows_wave(stage, dvt, 1.0f, dV + row * D, pb.Tk - k0w, lane);
+  };
+
+  // the copy cursor: item ordinal dk (item di), next tile dqt
+  int dk = 0;
+  Item di = item_at(0);
+  int dqt = di.qt0;
+  auto copy_next = [&](uint16_t* b) {
+    while (di.k0 >= 0 && dqt > di.qt1) {
+      di = item_at(++dk);
+      dqt = di.qt0;
+    }
+    if (di.k0 < 0) return false;
+    load_tile(di.n, dqt, b);
+    ++dqt;
+    return true;
+  };
+
+  Item ci = item_at(0);
+  if (ci.k0 < 0) return;
+  bf16x8 kf[4], vf[4];
+  load_kv(ci, kf, vf);
+  const bool c0 = copy_next(B0);
+  const bool c1 = c0 && copy_next(B1);
+  if (c1)
+    wait_all_but_one();
+  else
+    wait_vm();
+  __syncthreads();
+
+  // One tile position of item ci: copy the position two ahead into nxt
+  // (possibly the next item's), compute tile qt from cur.
+  f32x16 dvt[2], dkt[2];
+  auto step = [&](int qt, const uint16_t* cur, uint16_t* nxt) {
+    const bool more = copy_next(nxt);
+    const int q0 = qt * QT, k0w = ci.k0 + 32 * w;
+    dkdv_tile(cur, cur + QT * D, ls_of(cur), es_of(cur), kf, vf, dvt, dkt, sw, pb.sl2, g,
+              needs_mask(q0, q0 + QT - 1, k0w, k0w + 31, pb), q0, queries_of(k0w + c, pb));
+    if (more)
+      wait_all_but_one();
+    else
+      wait_vm();
+    __syncthreads();
+  };
+
+  // Before each tile position: if item ci has no tile left, store its dK and
+  // dV and move on to the next item with tiles (loading its K and V rows).
+  // False when the workgroup's items are done.
+  int ck = 0, qt = ci.qt0;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    dvt[e] = zero16();
+    dkt[e] = zero16();
+  }
+  auto advance = [&]() {
+    while (qt > ci.qt1) {
+      store_item(ci, dkt, dvt);
+      ci = item_at(++ck);
+      if (ci.k0 < 0) return false;
+      load_kv(ci, kf, vf);
+      qt = ci.qt0;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        dvt[e] = zero16();
+        dkt[e] = zero16();
+      }
+    }
+    return true;
+  };
+  // The ring goes B0, B1, B2 position by position, across item boundaries.
+  for (;;) {
+    if (!advance()) break;
+    step(qt++, B0, B2);
+    if (!advance()) break;
+    step(qt++, B1, B0);
+    if (!advance()) break;
+    step(qt++, B2, B1);
+  }
+}
+
 }  // namespace
+
+// Compute units of the device `stream` runs on (cached per device; 0 if the
+// runtime cannot say).
+int cu_count(hipStream_t stream) {
+  static int cache[64];
+  int dev = 0;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
 
 hipError_t launch_bwd_dkdv_d64(const TensorArg& q, const TensorArg& k, const TensorArg& v,
                                const TensorArg& dO, const float* lse, const float* delta,
@@ -345,8 +602,24 @@ hipError_t launch_bwd_dkdv_d64(const TensorArg& q, const TensorArg& k, const Ten
   constexpr int NW = 4;
   (void)lse;  // the seeds in the workspace carry lse
   const Problem pb = make_problem(p);
-  const long long blocks = (long long)pb.N * ((p.Tk + 32 * NW - 1) / (32 * NW));
-  return launch_kernel(attn_bwd_dkdv64<NW>, blocks, 64 * NW, stream, view_of(q), view_of(k),
+  const long long items = (long long)pb.N * ((p.Tk + 32 * NW - 1) / (32 * NW));
+  const long long slots = 2LL * cu_count(stream);
+  // dense [B][H][T][64] tensors and more items than slots: the persistent
+  // grid, one workgroup per slot, in eight groups of heads (one per XCD)
+  // when the heads and the grid split evenly
+  auto dense = [&](const TensorArg& t, long long T) {
+    return t.st == kD && t.sh == T * kD && t.sb == (long long)p.H * T * kD;
+  };
+  if (slots > 0 && items > slots && dense(q, p.Tq) && dense(dO, p.Tq) && dense(k, p.Tk) &&
+      dense(v, p.Tk) && dense(dk, p.Tk) && dense(dv, p.Tk)) {
+    const int X = (pb.N % 8 == 0 && slots % 8 == 0) ? 8 : 1;
+    const int R = (int)(slots / X);
+    auto P = [](const TensorArg& t) { return static_cast<const uint16_t*>(t.data); };
+    auto W = [](const TensorArg& t) { return const_cast<uint16_t*>(static_cast<const uint16_t*>(t.data)); };
+    return launch_kernel(attn_bwd_dkdv64p<NW>, slots, 64 * NW, stream, P(q), P(k), P(v), P(dO),
+                         delta, W(dk), W(dv), pb, (int)items, R, X);
+  }
+  return launch_kernel(attn_bwd_dkdv64<NW>, items, 64 * NW, stream, view_of(q), view_of(k),
                        view_of(v), view_of(dO), delta, view_of(dk), view_of(dv), pb);
 }
 
