@@ -54,7 +54,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 # / 8 cycles x 2.4 GHz exponentials per second.
 PEAK_EXP_PER_S = 256 * 4 * 64 / 8 * 2.4e9
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")  # traffic_<workload>.json
-KERNEL_SOURCES = ["attn_bf16.hip", "attn_d64.hip", "attn_common.h"]
+KERNEL_SOURCES = ["attn_bf16.hip", "attn_d64.hip", "attn_d128.hip", "attn_common.h"]
 FLUSH_BYTES = 1 << 30
 
 

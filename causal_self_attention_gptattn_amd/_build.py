@@ -11,7 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgptattn.so")
-SOURCES = ["gptattn_api.hip", "attn_bf16.hip", "attn_d64.hip", "attn_decode.hip", "attn_f32.hip"]
+SOURCES = ["gptattn_api.hip", "attn_bf16.hip", "attn_d64.hip", "attn_d128.hip", "attn_decode.hip",
+           "attn_f32.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -963,6 +963,10 @@ hipError_t launch_bwd_dkdv_bf16(const TensorArg& q, const TensorArg& k, const Te
   // shape, 256 keys: 23.5 against 20.0 us)
   if (p.D == 64 && !drop && p.Tk > 256)
     return launch_bwd_dkdv_d64(q, k, v, dO, lse, delta, dk, dv, p, stream);
+  // head size 128 without dropout, dense tensors, more 128-key items than
+  // compute units: the persistent 128-key kernel
+  if (dkdv_d128_applies(q, k, v, dO, dk, dv, p, stream))
+    return launch_bwd_dkdv_d128(q, k, v, dO, delta, dk, dv, p, stream);
   const Problem pb = make_problem(p);
   const long long blocks = (long long)pb.N * ((p.Tk + kKBN16 - 1) / kKBN16);
 #define GPTATTN_DKDV16(D_, DROP_)                                                               \

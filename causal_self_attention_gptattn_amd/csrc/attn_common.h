@@ -374,7 +374,7 @@ struct TileDMA {
     rowb = (uint32_t)(st * 2);
     goff = (uint32_t)row * rowb + 16u * (uint32_t)(slot ^ swz_key<D, W16>(row));
     gstep = (uint32_t)RSTEP * rowb;
-    wofs = (tid & ~63) * 8;
+    wofs = __builtin_amdgcn_readfirstlane(tid >> 6) * 512;  // uniform: the copy writes through M0
   }
 
   // src: first element of the tile (uniform); lds: the LDS tile.
@@ -422,6 +422,14 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 // iteration would otherwise wait for that iteration's tile copies).
 __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// s_waitcnt vmcnt(N), the other counters left alone, as an instruction the
+// compiler's own wait insertion takes into account.
+template <int N>
+__device__ __forceinline__ void wait_vm_upto() {
+  static_assert(N >= 0 && N < 16, "vmcnt field");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // ---------------------------------------------------------------------------
 // Epilogue: a wave's 32 x D block of results, held in the MFMA result layout
 // (lane (c, g) holds, for row c, columns 32e + 8u + 4g + i in acc[e][4u + i]),
@@ -432,6 +440,16 @@ __device__ __forceinline__ void wait_vm() { __builtin_amdgcn_s_waitcnt(0x0F70); 
 // `rows_valid` are not written.  lds: this wave's region, 16 * (D + 8)
 // elements, not in use by any other wave.
 // ---------------------------------------------------------------------------
+// The LDS accesses of one wave are carried out in program order; a fence at
+// wavefront scope keeps the compiler from moving them across this point.  So
+// a wave that stages data in an LDS area of its own needs no workgroup
+// barrier between writing and reading it back.
+__device__ __forceinline__ void wave_lds_order() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int D>
 __device__ __forceinline__ void store_rows(uint16_t* lds, const f32x16* acc, float mul,
                                            uint16_t* out, long long st, int rows_valid, int lane) {

@@ -178,14 +178,6 @@ __device__ __forceinline__ void dkdv_tile(const uint16_t* q, const uint16_t* d, 
   }
 }
 
-// s_waitcnt vmcnt(N), the other counters left alone, as an instruction the
-// compiler's own wait insertion takes into account.
-template <int N>
-__device__ __forceinline__ void wait_vm_upto() {
-  static_assert(N >= 0 && N < 16, "vmcnt field");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
-}
-
 // Workgroup = NW waves x 32 keys of one head; walks the 64-query tiles that
 // see its keys, from the diagonal to the end, through a ring of three LDS
 // buffers: the copy of tile t + 2 is issued as tile t starts, so a copy has
@@ -338,15 +330,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv64(
 
 
 // store_rows (attn_common.h) for a staging area that only the calling wave
-// uses: the LDS accesses of one wave are carried out in program order, so a
-// fence at wavefront scope (it keeps the compiler from moving LDS accesses
-// across it) replaces the workgroup barriers, and the waves of a workgroup
-// store their rows independently.
-__device__ __forceinline__ void wave_lds_order() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+// uses: wave_lds_order replaces the workgroup barriers, and the waves of a
+// workgroup store their rows independently.
 
 __device__ __forceinline__ void store_rows_wave(uint16_t* lds, const f32x16* acc, float mul,
                                                 uint16_t* out, int rows_valid, int lane) {
@@ -580,8 +565,6 @@ __global__ __launch_bounds__(64 * NW, 2) void attn_bwd_dkdv64p(
 
 }  // namespace
 
-// Compute units of the device `stream` runs on (cached per device; 0 if the
-// runtime cannot say).
 int cu_count(hipStream_t stream) {
   static int cache[64];
   int dev = 0;
@@ -607,9 +590,7 @@ hipError_t launch_bwd_dkdv_d64(const TensorArg& q, const TensorArg& k, const Ten
   // dense [B][H][T][64] tensors and more items than slots: the persistent
   // grid, one workgroup per slot, in eight groups of heads (one per XCD)
   // when the heads and the grid split evenly
-  auto dense = [&](const TensorArg& t, long long T) {
-    return t.st == kD && t.sh == T * kD && t.sb == (long long)p.H * T * kD;
-  };
+  auto dense = [&](const TensorArg& t, long long T) { return dense_bhtd(t, p.H, T, kD); };
   if (slots > 0 && items > slots && dense(q, p.Tq) && dense(dO, p.Tq) && dense(k, p.Tk) &&
       dense(v, p.Tk) && dense(dk, p.Tk) && dense(dv, p.Tk)) {
     const int X = (pb.N % 8 == 0 && slots % 8 == 0) ? 8 : 1;

@@ -47,6 +47,25 @@ hipError_t launch_bwd_dkdv_d64(const TensorArg& q, const TensorArg& k, const Ten
                                const TensorArg& dk, const TensorArg& dv, const ProblemArg& p,
                                hipStream_t stream);
 
+// Head size 128 without dropout, dense tensors, more (head, 128-key block)
+// items than compute units: the persistent dK/dV kernel (attn_d128.hip).
+bool dkdv_d128_applies(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                       const TensorArg& dO, const TensorArg& dk, const TensorArg& dv,
+                       const ProblemArg& p, hipStream_t stream);
+hipError_t launch_bwd_dkdv_d128(const TensorArg& q, const TensorArg& k, const TensorArg& v,
+                                const TensorArg& dO, const float* delta, const TensorArg& dk,
+                                const TensorArg& dv, const ProblemArg& p, hipStream_t stream);
+
+// Compute units of the device `stream` runs on (cached per device; 0 if the
+// runtime cannot say).
+int cu_count(hipStream_t stream);
+
+// A [B][H][T][D] tensor laid out densely (rows of D contiguous elements,
+// heads of T rows, batches of H heads).
+inline bool dense_bhtd(const TensorArg& t, int H, long long T, int D) {
+  return t.st == D && t.sh == T * D && t.sb == (long long)H * T * D;
+}
+
 // Short query blocks (Tq <= 4, Tk >= 64, no dropout, bf16): one workgroup per
 // head streams the keys (attn_decode.hip).  launch_fwd_bf16 routes such
 // problems here itself.

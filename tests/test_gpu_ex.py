@@ -266,9 +266,9 @@ def test_autograd_with_a_gradient_pooled_over_positions():
            "dv": to64(v.grad)}
     compare(got, ref, "bf16", label="pooled-gradient autograd")
 
-# (B, H, Tq, Tk, offset, window): head-size-64 backward problems with more
-# (head, 128-key block) items than the GPU has workgroup slots, which take the
-# persistent dK/dV grid when the tensors are dense
+# (B, H, Tq, Tk, offset, window): backward problems with more (head, 128-key
+# block) items than the GPU has workgroup slots, which take the persistent
+# dK/dV grids when the tensors are dense
 PERSISTENT = [
     (3, 64, 1000, 1000, 0, 0),     # 192 heads (eight groups of heads), ragged last block
     (6, 25, 520, 520, 0, 0),       # 150 heads: not a multiple of 8, one group
@@ -278,17 +278,18 @@ PERSISTENT = [
 ]
 
 
+@pytest.mark.parametrize("D", [64, 128])
 @pytest.mark.parametrize("B,H,Tq,Tk,off,win", PERSISTENT)
-def test_dkdv_persistent_grid(B, H, Tq, Tk, off, win):
-    """The persistent dK/dV grid (dense tensors) gives bit for bit what the
-    one-workgroup-per-item kernel gives (the same problem with dK and dV
-    written through row-padded views, which that kernel serves), and matches
-    the oracle on sampled heads, including keys no query sees (zero
-    gradients)."""
+def test_dkdv_persistent_grid(B, H, Tq, Tk, off, win, D):
+    """The persistent dK/dV grids (dense tensors) against the oracle on
+    sampled heads, and against the one-workgroup-per-item kernels, which
+    serve the same problem with dK and dV written through row-padded views:
+    bit for bit at D = 64 (the same arithmetic), within the bf16 tolerance
+    at D = 128 (the one-shot kernel adds lse to the scaled scores instead of
+    seeding the score accumulator).  Keys no query sees get zero gradients."""
     dev = need_gpu()
-    D = 64
-    say("persistent dK/dV", B, H, Tq, Tk, off, win)
-    inp = shifted_inputs(B, H, Tq, Tk, D, "bf16", seed=B * H + Tk)
+    say("persistent dK/dV", B, H, Tq, Tk, off, win, D)
+    inp = shifted_inputs(B, H, Tq, Tk, D, "bf16", seed=B * H + Tk + D)
     q, k, v, do = (inp[n].to(dev) for n in ("q", "k", "v", "do"))
     sc = inp["scale"]
     o, lse = G.fwd_ex(q, k, v, sc, off, win)
@@ -298,14 +299,20 @@ def test_dkdv_persistent_grid(B, H, Tq, Tk, off, win):
     dk2, dv2 = (t[..., :D] for t in pad)
     G.bwd_ex(q, k, v, o, do, lse, sc, off, win, dk=dk2, dv=dv2)
     torch.cuda.synchronize()
-    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
-    got = {"o": to64(o), "lse": to64(lse), "dq": to64(dq), "dk": to64(dk), "dv": to64(dv)}
-    heads = sample_heads(B, H, 4, seed=Tq)
     if Tq < Tk - off:  # keys past every query: exactly zero
         assert not dk[:, :, Tq + off:].any() and not dv[:, :, Tq + off:].any()
-    compare(got, run_oracle(inp, heads, offset=off, window=win), "bf16", heads,
-            label="persistent dK/dV B=%d H=%d Tq=%d Tk=%d off=%d win=%d" % (B, H, Tq, Tk, off,
-                                                                            win))
+    heads = sample_heads(B, H, 4, seed=Tq)
+    ref = run_oracle(inp, heads, offset=off, window=win)
+    label = "persistent dK/dV B=%d H=%d Tq=%d Tk=%d off=%d win=%d D=%d" % (B, H, Tq, Tk, off,
+                                                                           win, D)
+    got = {"o": to64(o), "lse": to64(lse), "dq": to64(dq), "dk": to64(dk), "dv": to64(dv)}
+    compare(got, ref, "bf16", heads, label=label)
+    if D == 64:
+        assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    else:
+        assert not torch.isnan(dk2).any() and not torch.isnan(dv2).any()
+        got2 = dict(got, dk=to64(dk2), dv=to64(dv2))
+        compare(got2, ref, "bf16", heads, label=label + " (one-shot kernel)")
 
 
 def test_decode_beyond_the_decode_grid_runs_on_the_tile_kernel():
