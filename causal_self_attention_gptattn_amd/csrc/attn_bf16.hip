@@ -181,8 +181,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd(
 
   bf16x8 qf[DS];  // this lane's query row (zero past Tq)
   {
+    // (the row block's start taken as the uniform value it is, so the load
+    // needs no loop over distinct descriptors)
+    const int q0u = __builtin_amdgcn_readfirstlane(q0w);
     RowBlock qr;
-    qr.init(head_of(Q, n, pb.H) + (long long)q0w * Q.st, pb.Tq - q0w, Q.st, c);
+    qr.init(head_of(Q, n, pb.H) + (long long)q0u * Q.st, pb.Tq - q0u, Q.st, c);
 #pragma unroll
     for (int s = 0; s < DS; ++s) qf[s] = __builtin_bit_cast(bf16x8, qr.load(16 * s + 8 * g));
   }
@@ -370,10 +373,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void attn_bwd_dq(
   bf16x8 qf[DS], df[DS];  // this lane's query rows of Q and dO (zero past Tq)
   float dpart = 0.0f;
   {
+    const int q0u = __builtin_amdgcn_readfirstlane(q0w);  // uniform row block start
     RowBlock qr, dr, orr;
-    qr.init(head_of(Q, n, pb.H) + (long long)q0w * Q.st, pb.Tq - q0w, Q.st, c);
-    dr.init(head_of(dO, n, pb.H) + (long long)q0w * dO.st, pb.Tq - q0w, dO.st, c);
-    orr.init(head_of(O, n, pb.H) + (long long)q0w * O.st, pb.Tq - q0w, O.st, c);
+    qr.init(head_of(Q, n, pb.H) + (long long)q0u * Q.st, pb.Tq - q0u, Q.st, c);
+    dr.init(head_of(dO, n, pb.H) + (long long)q0u * dO.st, pb.Tq - q0u, dO.st, c);
+    orr.init(head_of(O, n, pb.H) + (long long)q0u * O.st, pb.Tq - q0u, O.st, c);
     u32x4 ou[DS];
 #pragma unroll
     for (int s = 0; s < DS; ++s) {
@@ -531,7 +535,7 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void attn_bwd_dkdv16w(
   __shared__ __attribute__((aligned(16))) float Es[2][BM];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int bid = blockIdx.x;
   const int kb = bid / pb.N;
@@ -745,7 +749,7 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bwd_dq16(
   __shared__ __attribute__((aligned(16))) uint16_t V0[BN * D], V1[BN * D];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6;
+  const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int bid = blockIdx.x;
   const int qb = nqb - 1 - bid / pb.N;
