@@ -17,7 +17,10 @@ workspace vectors) from the 256 MB last-level cache, so every step reads
 its inputs from HBM.  Each timed step carries three events on the launch
 stream (before the forward, before the dominant kernel, after the step):
 the step time, and the dominant kernel's time for the roofline, both
-measured live over the timed steps.  The warm figure (steps back to back,
+measured live over the timed steps.  The events are HIP events created
+with hipEventDisableSystemFence: a default event fences at system scope
+when recorded (a cache writeback and invalidation), which would slow the
+kernel after it.  The warm figure (steps back to back,
 no flush, wall clock) is reported beside it.  A separate pass with an event
 at every launch boundary gives the per-kernel table.  The clock (sclk) is
 sampled with rocm-smi while the same flushed steps keep running right after
@@ -56,6 +59,65 @@ PEAK_EXP_PER_S = 256 * 4 * 64 / 8 * 2.4e9
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")  # traffic_<workload>.json
 KERNEL_SOURCES = ["attn_bf16.hip", "attn_d64.hip", "attn_d128.hip", "attn_common.h"]
 FLUSH_BYTES = 1 << 30
+# hipEventDisableSystemFence (hip_runtime_api.h): record the event without
+# the system-scope fence a default event performs, a cache writeback and
+# invalidation that slows whatever kernel follows it
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
+
+
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence,
+    with torch.cuda.Event's record / elapsed_time interface.  A default
+    event (torch's) fences at system scope when recorded: one recorded
+    between two kernels writes back and invalidates the caches, which costs
+    the step about 4 us at the GPT-2 shape and slows the kernel after it."""
+
+    _hip = None
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p),
+                                                    ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            cls._hip = hip
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+
+        self.ev = ctypes.c_void_p()
+        rc = self._lib().hipEventCreateWithFlags(ctypes.byref(self.ev),
+                                                 HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if rc != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed (%d)" % rc)
+
+    def record(self, stream):
+        import ctypes
+
+        rc = self._lib().hipEventRecord(self.ev, ctypes.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % rc)
+
+    def elapsed_time(self, end):
+        """Milliseconds from this event to `end` (both recorded and done)."""
+        import ctypes
+
+        ms = ctypes.c_float()
+        rc = self._lib().hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
 
 
 def unit_flops(N, T, D):
@@ -241,12 +303,12 @@ def time_steps(step, steps, warmup, stream):
 
     for _ in range(warmup):
         step()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev = [TimingEvent() for _ in range(2)]
     ev[0].record(stream)
     for _ in range(steps):
         step()
     ev[1].record(stream)
-    ev[1].synchronize()
+    torch.cuda.synchronize()
     return ev[0].elapsed_time(ev[1]) / steps
 
 
@@ -343,7 +405,7 @@ def per_kernel_pass(step, steps, stream, flush):
     boundary, the caches flushed before each step (outside the events)."""
     import torch
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    ev = [[TimingEvent() for _ in range(4)] for _ in range(steps)]
     for e in ev:
         if flush is not None:
             flush.fill_(1)
@@ -542,7 +604,7 @@ def main():
     # timed steps: caches flushed before each (outside the events); events
     # before the forward, before the dominant kernel and after the step
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
     for e in evs:

@@ -70,6 +70,18 @@ def test_source_hash_ignores_comments_only(bench):
     assert bench.code_of(a) == bench.code_of(b) != bench.code_of(c)
 
 
+def test_timing_event_flag_matches_the_hip_header(bench):
+    """The timing events skip the system-scope fence: the flag is the one
+    HIP's runtime header defines for that."""
+    import re
+
+    header = "/opt/rocm/include/hip/hip_runtime_api.h"
+    if not os.path.exists(header):
+        pytest.skip("no HIP runtime header here")
+    m = re.search(r"#define\s+hipEventDisableSystemFence\s+(0x[0-9a-fA-F]+)", open(header).read())
+    assert m and int(m.group(1), 16) == bench.HIP_EVENT_DISABLE_SYSTEM_FENCE
+
+
 def test_more_than_one_gpu_is_refused():
     out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                          capture_output=True, text=True, timeout=120)
