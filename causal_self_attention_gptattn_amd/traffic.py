@@ -36,8 +36,9 @@ def _per_kernel_kib(path, counter):
                 continue
             # the launch a kernel serves: attn_bwd_dq16<...>, attn_bwd_dkdv16w<...>
             # (16-row waves) and the head-size-64 kernels (attn_bwd_dkdv64<...>,
-            # attn_bwd_dkdv64p<...>) count as attn_bwd_dq / attn_bwd_dkdv / attn_fwd
-            m = re.search(r"::(attn_[a-z_]+?)(?:16w?|64p?)?<", row["Kernel_Name"]) or re.search(
+            # attn_bwd_dkdv64p<...>, attn_bwd_dkdv128p<...>) count as attn_bwd_dq /
+            # attn_bwd_dkdv / attn_fwd
+            m = re.search(r"::(attn_[a-z_]+?)(?:16w?|64p?|128p)?<", row["Kernel_Name"]) or re.search(
                 r"(__amd_rocclr_copyBuffer)", row["Kernel_Name"])
             if not m:
                 continue

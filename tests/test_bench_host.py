@@ -101,6 +101,7 @@ def test_traffic_counters_are_keyed_by_launch(tmp_path):
             ("void gptattn::(anonymous namespace)::attn_bwd_dkdv16w<128, false>(...)", 50.0),
             ("void gptattn::(anonymous namespace)::attn_bwd_dkdv64<4>(...)", 60.0),
             ("void gptattn::(anonymous namespace)::attn_bwd_dkdv64p<4>(...)", 70.0),
+            ("void gptattn::(anonymous namespace)::attn_bwd_dkdv128p<8>(...)", 80.0),
             ("__amd_rocclr_copyBuffer", 7.0)]
     path = tmp_path / "c.csv"
     with open(path, "w") as f:
@@ -108,7 +109,7 @@ def test_traffic_counters_are_keyed_by_launch(tmp_path):
         for name, v in rows:
             f.write('"%s",FETCH_SIZE,%g\n' % (name, v))
     got = traffic._per_kernel_kib(str(path), "FETCH_SIZE")
-    assert got == {"attn_fwd": 10.0, "attn_bwd_dq": 30.0, "attn_bwd_dkdv": (30.0 + 50.0 + 60.0 + 70.0) / 4,
+    assert got == {"attn_fwd": 10.0, "attn_bwd_dq": 30.0, "attn_bwd_dkdv": (30.0 + 50.0 + 60.0 + 70.0 + 80.0) / 5,
                    "__amd_rocclr_copyBuffer": 7.0}
 
 
