@@ -206,12 +206,32 @@ def cpu_model():
     return platform.processor() or platform.machine()
 
 
+def parse_smi(rec):
+    """sclk readings (MHz) and power readings (W) of the first card in a
+    `rocm-smi --showclocks --showpower --json` record."""
+    card = next(iter(rec.values()), {}) if isinstance(rec, dict) else {}
+    sclk, power = [], []
+    for k_, v_ in card.items():
+        key = k_.lower()
+        if "sclk" in key and "speed" in key:
+            digits = "".join(ch for ch in str(v_) if ch.isdigit())
+            if digits:
+                sclk.append(int(digits))
+        elif "power" in key and "(w)" in key:
+            try:
+                power.append(float(v_))
+            except (TypeError, ValueError):
+                pass
+    return sclk, power
+
+
 class ClockSampler:
-    """Polls rocm-smi for sclk (and power) in a background thread while the
+    """Polls rocm-smi for sclk and power in a background thread while the
     GPU works; best effort (no samples when the tool is missing)."""
 
     def __init__(self, enabled=True):
         self.samples = []
+        self.power = []
         self.enabled = enabled
         self._stop = threading.Event()
         self._t = None
@@ -224,12 +244,9 @@ class ClockSampler:
                 rec = json.loads(out)
             except Exception:  # noqa: BLE001 -- a diagnostic, never fatal
                 return
-            card = next(iter(rec.values()), {}) if isinstance(rec, dict) else {}
-            for k_, v_ in card.items():
-                if "sclk" in k_.lower() and "speed" in k_.lower():
-                    digits = "".join(ch for ch in str(v_) if ch.isdigit())
-                    if digits:
-                        self.samples.append(int(digits))
+            sclk, power = parse_smi(rec)
+            self.samples += sclk
+            self.power += power[:1]
 
     def __enter__(self):
         if self.enabled:
@@ -681,6 +698,8 @@ def main():
         print("bench: oracle CPU baseline (%.0f s budget)" % args.cpu_budget,
               file=sys.stderr, flush=True)
         base = cpu_baseline(inp, args.cpu_budget)
+        # GPU speed-up over the oracle on the same workload (algorithmic rates)
+        base["gpu_speedup"] = round(value / base["value"], 1)
 
     sclk = clocks.samples
     out = {
@@ -721,11 +740,21 @@ def main():
             "unit": rl["unit"],
             "frac": round(rl["frac"], 4),
             "traffic": measured_traffic(dom, w.name),
+            # the algorithmic work of one launch, against which traffic compares
+            "alg_bytes": table[dom]["bytes"],
+            "alg_flops": table[dom]["flops"],
         },
+        # forward and backward separately (the per-kernel pass; backward =
+        # dQ + dK/dV launches)
+        "fwd_ms": round(pk[0], 5),
+        "bwd_ms": round(pk[1] + pk[2], 5),
         "cpu_baseline": base,
         "sclk_mhz_under_load": {"samples": len(sclk),
                                 "median": int(np.median(sclk)) if sclk else None,
                                 "min": min(sclk) if sclk else None},
+        "power_w_under_load": {"samples": len(clocks.power),
+                               "median": round(float(np.median(clocks.power)), 1)
+                               if clocks.power else None},
         "configs": cfgs,
         "variants": var,
     }

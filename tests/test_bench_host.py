@@ -82,6 +82,18 @@ def test_timing_event_flag_matches_the_hip_header(bench):
     assert m and int(m.group(1), 16) == bench.HIP_EVENT_DISABLE_SYSTEM_FENCE
 
 
+def test_rocm_smi_record_parsing(bench):
+    """sclk and power come out of rocm-smi's JSON record of the first card."""
+    rec = {"card0": {"sclk clock speed:": "(1972Mhz)", "sclk clock level:": "1",
+                     "fclk clock speed:": "(2000Mhz)",
+                     "Current Socket Graphics Package Power (W)": "871.0",
+                     "Card Series": "AMD Instinct MI355X"},
+           "card1": {"sclk clock speed:": "(100Mhz)"}}
+    assert bench.parse_smi(rec) == ([1972], [871.0])
+    assert bench.parse_smi({}) == ([], [])
+    assert bench.parse_smi([]) == ([], [])
+
+
 def test_more_than_one_gpu_is_refused():
     out = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                          capture_output=True, text=True, timeout=120)
