@@ -225,6 +225,17 @@ def parse_smi(rec):
     return sclk, power
 
 
+def parse_amdsmi_power(rec):
+    """Socket power (W) of the first GPU in an `amd-smi metric --power --json`
+    record."""
+    try:
+        gpus = rec["gpu_data"] if isinstance(rec, dict) else rec
+        sp = gpus[0]["power"]["socket_power"]
+        return [float(sp["value"] if isinstance(sp, dict) else sp)]
+    except (KeyError, IndexError, TypeError, ValueError):
+        return []
+
+
 class ClockSampler:
     """Polls rocm-smi for sclk and power in a background thread while the
     GPU works; best effort (no samples when the tool is missing)."""
@@ -246,6 +257,13 @@ class ClockSampler:
                 return
             sclk, power = parse_smi(rec)
             self.samples += sclk
+            if not power:
+                try:
+                    out = subprocess.run(["amd-smi", "metric", "--power", "--json"],
+                                         capture_output=True, text=True, timeout=10).stdout
+                    power = parse_amdsmi_power(json.loads(out))
+                except Exception:  # noqa: BLE001 -- a diagnostic, never fatal
+                    power = []
             self.power += power[:1]
 
     def __enter__(self):

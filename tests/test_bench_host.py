@@ -92,6 +92,11 @@ def test_rocm_smi_record_parsing(bench):
     assert bench.parse_smi(rec) == ([1972], [871.0])
     assert bench.parse_smi({}) == ([], [])
     assert bench.parse_smi([]) == ([], [])
+    rec = {"gpu_data": [{"gpu": 0, "power": {"socket_power": {"value": 248, "unit": "W"},
+                                             "gfx_voltage": "N/A"}}]}
+    assert bench.parse_amdsmi_power(rec) == [248.0]
+    assert bench.parse_amdsmi_power({"gpu_data": []}) == []
+    assert bench.parse_amdsmi_power({}) == []
 
 
 def test_more_than_one_gpu_is_refused():
