@@ -275,6 +275,8 @@ PERSISTENT = [
     (1, 72, 100, 1000, 0, 0),      # keys 100..999 seen by no query: empty items
     (2, 40, 1024, 1024, 0, 200),   # banded
     (1, 96, 300, 900, 600, 0),     # queries appended after a 600-token context
+    (2, 100, 257, 257, 0, 0),      # just above the 256-key routing threshold
+    (8, 96, 1024, 1024, 0, 0),     # 768 heads: long item lists per workgroup
 ]
 
 
