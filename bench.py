@@ -442,12 +442,14 @@ class Step:
 LAUNCHES = ("attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv")
 
 
-def per_kernel_pass(step, steps, stream, flush, keep_busy=0):
+def per_kernel_pass(step, steps, stream, flush, keep_busy=0, events=None):
     """Each kernel's average duration (ms) with an event at every launch
     boundary, the caches flushed before each step (outside the events).
     With keep_busy > 0, that many more (untimed) steps are queued behind the
-    pass, and the results are read while the GPU runs them."""
-    ev = [[TimingEvent() for _ in range(4)] for _ in range(steps)]
+    pass, and the results are read while the GPU runs them.  `events`:
+    steps x 4 TimingEvents created beforehand (else created here)."""
+    ev = events if events is not None else [[TimingEvent() for _ in range(4)]
+                                            for _ in range(steps)]
     for e in ev:
         if flush is not None:
             flush.fill_(1)
@@ -472,9 +474,12 @@ def workload_configs(G, dev, stream, steps, flush):
     for name, w in W.WORKLOADS.items():
         q, k, v, do = gpu_inputs(w.B, w.H, w.T, w.D, w.dtype, dev)
         st = Step(G, q, k, v, do, W.default_scale(w.D), stream)
-        for _ in range(3):
+        evs = [[TimingEvent() for _ in range(4)] for _ in range(steps)]
+        # flushed warm-up running on into the pass (no idle gap, see main)
+        for _ in range(20):
+            flush.fill_(1)
             st()
-        ks = per_kernel_pass(st, steps, stream, flush)
+        ks = per_kernel_pass(st, steps, stream, flush, events=evs)
         ms = sum(ks)
         flops = 6 * unit_flops(w.N, w.T, w.D)
         table = kernel_table(w.N, w.T, w.D, 4 if w.dtype == "f32" else 2)
@@ -638,20 +643,21 @@ def main():
     table = kernel_table(N, T, D)
     flops = 6 * unit_flops(N, T, D)
 
-    # warm-up in the pattern of the timed steps (flush, step): the GPU's clock
-    # takes tens of milliseconds of this load to settle (the step time dips
-    # and recovers over the first ~20 ms), and a training loop runs at the
-    # settled clock
+    # Every timing event is created up front: creating them later would
+    # leave the GPU idle in between, and its clock would drop.
+    pk_evs = [[TimingEvent() for _ in range(4)] for _ in range(args.steps)]
+    evs = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
+
+    # warm-up in the pattern of the timed steps (flush, step), running on into
+    # the per-kernel pass without a pause
     print("bench: warmup %d steps" % args.warmup, file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         flush.fill_(1)
         step()
-    torch.cuda.synchronize(dev)
 
     # per-kernel table: events at every launch boundary, caches flushed
     print("bench: per-kernel pass %d steps" % args.steps, file=sys.stderr, flush=True)
-    evs = [[TimingEvent() for _ in range(3)] for _ in range(args.steps)]
-    pk = per_kernel_pass(step, args.steps, stream, flush, keep_busy=10)
+    pk = per_kernel_pass(step, args.steps, stream, flush, keep_busy=10, events=pk_evs)
     dom_i = max(range(3), key=lambda i: pk[i])
     dom = LAUNCHES[dom_i]
 
