@@ -148,12 +148,28 @@ __device__ __forceinline__ void fwd_tile(const uint16_t* kb, const uint16_t* vb,
   }
 }
 
+// The item (index into the longest-first list of `items` workgroup items)
+// that workgroup b runs.  The dispatcher fills the CUs breadth-first, so
+// workgroups b, b + C, b + 2C, ... (C = `deal`, the CU count) share a CU;
+// dealing every other round of C items in reverse order pairs long items with
+// short ones on each CU.  Reversal is in groups of g (8 when the head count
+// is a multiple of 8), so an item keeps its workgroup's index mod 8 and a
+// head's workgroups stay on one XCD.  deal = 0: the list order itself.
+__device__ __forceinline__ int dealt_item(int b, int items, int deal, int g) {
+  if (deal <= 0) return b;
+  const int r = b / deal, p = b - r * deal, base = r * deal;
+  const int cnt = min(deal, items - base);
+  if ((r & 1) == 0 || cnt % g != 0) return b;
+  return base + (cnt / g - 1 - p / g) * g + p % g;
+}
+
 // Occupancy: four waves per SIMD at D = 64 (at most 128 registers), two at
 // D = 128 (fits without spilling; 1.6x faster than one wave at the GPT-3
 // shape).
 template <int D, bool DROP>
 __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd(
-    View Q, View K, View V, View O, float* __restrict__ LSE, Problem pb, int nqb) {
+    View Q, View K, View V, View O, float* __restrict__ LSE, Problem pb, int nqb, int deal,
+    int dealg) {
   constexpr int BM = kBM, BN = kBN;
   constexpr int LD = D + 8;     // row stride of the epilogue staging (padded)
   constexpr int DS = D / 16;    // k-steps of the score product
@@ -171,8 +187,10 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd(
   SwzLane<D> sw;
   sw.init(c, g, tr_rowoff(lane), tr_coloff(lane));
   const int bid = blockIdx.x;
-  const int qb = nqb - 1 - bid / pb.N;  // longest query blocks first
-  const int n = bid % pb.N;
+  // longest query blocks first, dealt over the CUs
+  const int item = dealt_item(bid, nqb * pb.N, deal, dealg);
+  const int qb = nqb - 1 - item / pb.N;
+  const int n = item % pb.N;
   const uint16_t* Kh = head_of(K, n, pb.H);
   const uint16_t* Vh = head_of(V, n, pb.H);
   const int q0 = qb * BM;
@@ -921,8 +939,14 @@ hipError_t launch_fwd_bf16(const TensorArg& q, const TensorArg& k, const TensorA
   const int nqb = (p.Tq + kBM - 1) / kBM;
   const long long blocks = (long long)pb.N * nqb;
   const bool drop = p.dropout > 0.0f;
+  // at D = 64 (four workgroups per CU) the longest-first list is dealt over
+  // the CUs (dealt_item); at D = 128 it runs in list order
+  const int cus = p.D == 64 ? cu_count(stream) : 0;
+  const int deal = cus > 0 && cus % 8 == 0 ? cus : 0;
+  const int dealg = pb.N % 8 == 0 ? 8 : 1;
 #define GPTATTN_FWD(D_, DROP_)                                                                  \
-  launch(attn_fwd<D_, DROP_>, blocks, stream, view(q), view(k), view(v), view(o), lse, pb, nqb)
+  launch(attn_fwd<D_, DROP_>, blocks, stream, view(q), view(k), view(v), view(o), lse, pb, nqb, \
+         deal, dealg)
   switch (p.D) {
     case 64: return drop ? GPTATTN_FWD(64, true) : GPTATTN_FWD(64, false);
     case 128: return drop ? GPTATTN_FWD(128, true) : GPTATTN_FWD(128, false);
