@@ -689,8 +689,8 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void attn_bwd_dkdv16w(
 }
 
 // ---------------------------------------------------------------------------
-// dQ at D = 64 with 16 queries per wave on the 16 x 16 x 32 product: 114
-// registers (126 with dropout), four waves per SIMD, workgroups of 64
+// dQ at D = 64 with 16 queries per wave on the 16 x 16 x 32 product: 124
+// registers (with or without dropout), four waves per SIMD, workgroups of 64
 // queries.  Lane (g, c) owns query c of the wave; S^T and dP^T come out with
 // rows = keys 4g + r of each 16-key block; dS^T of two blocks is packed into
 // one operand and dQ^T (rows = head dims 16m + 4g + r, columns = queries)
