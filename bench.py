@@ -442,12 +442,13 @@ class Step:
 LAUNCHES = ("attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv")
 
 
-def per_kernel_pass(step, steps, stream, flush, keep_busy=0, events=None):
+def per_kernel_pass(step, steps, stream, flush, keep_busy=0, events=None, step_times=None):
     """Each kernel's average duration (ms) with an event at every launch
     boundary, the caches flushed before each step (outside the events).
     With keep_busy > 0, that many more (untimed) steps are queued behind the
     pass, and the results are read while the GPU runs them.  `events`:
-    steps x 4 TimingEvents created beforehand (else created here)."""
+    steps x 4 TimingEvents created beforehand (else created here).  A list
+    passed as `step_times` receives each step's duration (ms)."""
     ev = events if events is not None else [[TimingEvent() for _ in range(4)]
                                             for _ in range(steps)]
     for e in ev:
@@ -462,12 +463,16 @@ def per_kernel_pass(step, steps, stream, flush, keep_busy=0, events=None):
             flush.fill_(1)
         step()
     ev[-1][3].synchronize()
+    if step_times is not None:
+        step_times.extend(e[0].elapsed_time(e[3]) for e in ev)
     return [sum(e[i].elapsed_time(e[i + 1]) for e in ev) / steps for i in range(3)]
 
 
 def workload_configs(G, dev, stream, steps, flush):
     """The pages' other workloads, timed like the main one (cold caches,
     events at every launch boundary)."""
+    import numpy as np
+
     from causal_self_attention_gptattn_amd import workloads as W
 
     out = {}
@@ -479,14 +484,18 @@ def workload_configs(G, dev, stream, steps, flush):
         for _ in range(20):
             flush.fill_(1)
             st()
-        ks = per_kernel_pass(st, steps, stream, flush, events=evs)
+        totals = []
+        ks = per_kernel_pass(st, steps, stream, flush, events=evs, step_times=totals)
         ms = sum(ks)
+        q1, med, q3 = (float(x) for x in np.percentile(totals, [25, 50, 75]))
         flops = 6 * unit_flops(w.N, w.T, w.D)
         table = kernel_table(w.N, w.T, w.D, 4 if w.dtype == "f32" else 2)
         rec = {"B": w.B, "H": w.H, "T": w.T, "D": w.D, "dtype": w.dtype,
                "ms_per_step": round(ms, 5), "alg_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
                "pct_of_bf16_mfma_peak": round(100.0 * flops / (ms * 1e-3) / 1e12
                                               / PEAK_BF16_TFLOPS, 2),
+               "step_ms_events": {"median": round(med, 5), "min": round(min(totals), 5),
+                                  "iqr": round(q3 - q1, 5)},
                "kernels_ms": {n: round(t, 5) for n, t in zip(LAUNCHES, ks)}}
         dom = max(range(3), key=lambda i: ks[i])
         rl = roofline(table[LAUNCHES[dom]]["flops"], table[LAUNCHES[dom]]["bytes"],

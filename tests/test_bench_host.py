@@ -155,3 +155,40 @@ def test_float32_tensor_bytes(bench):
     t16 = bench.kernel_table(4, 64, 16)["attn_fwd"]["bytes"]
     t32 = bench.kernel_table(4, 64, 16, 4)["attn_fwd"]["bytes"]
     assert t32 - t16 == 4 * (4 * 64 * 16 * 2)
+
+
+def test_per_kernel_pass_timing_with_fake_events(bench):
+    """The per-kernel pass on the CPU with stand-in events: each kernel's mean
+    is taken between the events at its launch boundaries, and each step's
+    duration runs from the first event to the last."""
+    clock = [0.0]
+
+    class Event:
+        def record(self, stream):
+            self.t = clock[0]
+
+        def elapsed_time(self, later):
+            return later.t - self.t
+
+        def synchronize(self):
+            pass
+
+    class Step:
+        def __init__(self):
+            self.n = 0
+
+        def launch(self, i):
+            clock[0] += (1.0, 2.0, 3.0)[i] + 0.5 * self.n
+            if i == 2:
+                self.n += 1
+
+        def __call__(self):
+            for i in range(3):
+                self.launch(i)
+
+    ev = [[Event() for _ in range(4)] for _ in range(4)]
+    totals = []
+    ks = bench.per_kernel_pass(Step(), 4, None, None, keep_busy=2, events=ev, step_times=totals)
+    # step s adds 0.5 * s to each of its three launches
+    assert ks == pytest.approx([1.75, 2.75, 3.75])
+    assert totals == pytest.approx([6.0, 7.5, 9.0, 10.5])
