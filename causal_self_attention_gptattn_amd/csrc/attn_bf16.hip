@@ -32,6 +32,10 @@
 //                 dQ^T += K^T dS^T.
 //   attn_bwd_dq16 the same at D = 64 with 16 queries per wave on the
 //                 16 x 16 x 32 product (four waves per SIMD instead of three).
+//                 Both dQ kernels run longest query blocks first; a problem
+//                 of eight or more rounds of the GPU's workgroup slots takes
+//                 its heads in groups (grouped_item), so that each head's K/V
+//                 tiles are re-read close together in time and stay cached.
 //   attn_bwd_dkdv16w  one workgroup = 64 keys of one head (4 waves x 16).
 //                 Walks the query tiles that see its keys with the
 //                 lane -> key layout: S = Q K^T and dP = dO V^T, then
@@ -161,6 +165,20 @@ __device__ __forceinline__ int dealt_item(int b, int items, int deal, int g) {
   const int cnt = min(deal, items - base);
   if ((r & 1) == 0 || cnt % g != 0) return b;
   return base + (cnt / g - 1 - p / g) * g + p % g;
+}
+
+// Query block qb and head n of workgroup b when heads are taken in groups of
+// hg (a multiple of 8, so a head's workgroups keep their index mod 8 and
+// stay on one XCD when N is a multiple of 8): a group's workgroups run
+// together, longest query blocks first, so each head's K/V tiles are re-read
+// close together in time.  hg >= N: one group, the plain longest-first list.
+struct QItem {
+  int qb, n;
+};
+__device__ __forceinline__ QItem grouped_item(int b, int N, int nqb, int hg) {
+  const int per = hg * nqb, gi = b / per, r = b - gi * per;
+  const int h0 = gi * hg, gn = min(hg, N - h0);
+  return QItem{nqb - 1 - r / gn, h0 + r % gn};
 }
 
 // Occupancy: four waves per SIMD at D = 64 (at most 128 registers), two at
@@ -341,7 +359,7 @@ __device__ __forceinline__ void dq_tile(const uint16_t* kb, const uint16_t* vb, 
 template <int D, bool DROP>
 __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void attn_bwd_dq(
     View Q, View K, View V, View O, View dO, const float* __restrict__ LSE, View dQ,
-    float* __restrict__ Delta, Problem pb, int nqb) {
+    float* __restrict__ Delta, Problem pb, int nqb, int hg) {
   constexpr int BM = kBM, BN = kBN;
   constexpr int LD = D + 8;
   constexpr int DS = D / 16;
@@ -359,8 +377,9 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 3 : 2) void attn_bwd_dq(
   SwzLane<D> sw;
   sw.init(c, g, tr_rowoff(lane), tr_coloff(lane));
   const int bid = blockIdx.x;
-  const int qb = nqb - 1 - bid / pb.N;
-  const int n = bid % pb.N;
+  const QItem qit = grouped_item(bid, pb.N, nqb, hg);
+  const int qb = qit.qb;
+  const int n = qit.n;
   const uint16_t* Kh = head_of(K, n, pb.H);
   const uint16_t* Vh = head_of(V, n, pb.H);
   const int q0 = qb * BM;
@@ -761,7 +780,7 @@ __device__ __forceinline__ void dq16_tile(const uint16_t* kb, const uint16_t* vb
 template <int D, bool DROP>
 __global__ __launch_bounds__(kThreads, 4) void attn_bwd_dq16(
     View Q, View K, View V, View O, View dO, const float* __restrict__ LSE, View dQ,
-    float* __restrict__ Delta, Problem pb, int nqb) {
+    float* __restrict__ Delta, Problem pb, int nqb, int hg) {
   constexpr int BM = kBM16, BN = kBN, NS = D / 32, NM = D / 16;
   __shared__ __attribute__((aligned(16))) uint16_t K0[BN * D], K1[BN * D];
   __shared__ __attribute__((aligned(16))) uint16_t V0[BN * D], V1[BN * D];
@@ -770,8 +789,9 @@ __global__ __launch_bounds__(kThreads, 4) void attn_bwd_dq16(
   const int lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 15, g = lane >> 4;
   const int bid = blockIdx.x;
-  const int qb = nqb - 1 - bid / pb.N;
-  const int n = bid % pb.N;
+  const QItem qit = grouped_item(bid, pb.N, nqb, hg);
+  const int qb = qit.qb;
+  const int n = qit.n;
   const uint16_t* Kh = head_of(K, n, pb.H);
   const uint16_t* Vh = head_of(V, n, pb.H);
   const int q0 = qb * BM;
@@ -963,14 +983,27 @@ hipError_t launch_bwd_dq_bf16(const TensorArg& q, const TensorArg& k, const Tens
   const int nqb = (p.Tq + kBM - 1) / kBM;
   const long long blocks = (long long)pb.N * nqb;
   const bool drop = p.dropout > 0.0f;
+  // Problems of at least eight rounds of the GPU's workgroup slots take their
+  // heads in balanced groups of about four rounds each (multiples of 8
+  // heads); smaller ones run the plain longest-first list (one group).
+  const int cus = cu_count(stream);
+  auto group_of = [&](int nq, int per_cu) {
+    const long long slots = (long long)cus * per_cu;
+    if (slots <= 0 || pb.N % 8 != 0 || (long long)pb.N * nq < 8 * slots) return pb.N;
+    const long long groups = ((long long)pb.N * nq + 4 * slots - 1) / (4 * slots);
+    const long long h = ((pb.N + groups - 1) / groups + 7) / 8 * 8;
+    return (int)(h < pb.N ? h : pb.N);
+  };
+  const int hg = group_of(nqb, 2);
 #define GPTATTN_DQ(D_, DROP_)                                                                   \
   launch(attn_bwd_dq<D_, DROP_>, blocks, stream, view(q), view(k), view(v), view(o), view(dO),  \
-         lse, view(dq), delta, pb, nqb)
+         lse, view(dq), delta, pb, nqb, hg)
   const int nqb16 = (p.Tq + kBM16 - 1) / kBM16;
   const long long blocks16 = (long long)pb.N * nqb16;
+  const int hg16 = group_of(nqb16, 4);
 #define GPTATTN_DQ16(D_, DROP_)                                                                 \
   launch(attn_bwd_dq16<D_, DROP_>, blocks16, stream, view(q), view(k), view(v), view(o),        \
-         view(dO), lse, view(dq), delta, pb, nqb16)
+         view(dO), lse, view(dq), delta, pb, nqb16, hg16)
   switch (p.D) {
     case 64: return drop ? GPTATTN_DQ16(64, true) : GPTATTN_DQ16(64, false);
     case 128: return drop ? GPTATTN_DQ(128, true) : GPTATTN_DQ(128, false);

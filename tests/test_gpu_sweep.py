@@ -118,6 +118,49 @@ def test_long_sequence_forward_rows(D):
         say("long T=%d D=%d rows %d: O err %.2e" % (T, D, i0, err_o))
 
 
+@pytest.mark.parametrize("B,H,T,D", [
+    (48, 12, 1024, 64),   # 576 heads x 16 query blocks: 9 rounds of the 16-query dQ kernel's slots
+    (256, 8, 256, 128),   # 2048 heads x 2 query blocks: 8 rounds of the 32-query dQ kernel's slots
+])
+def test_dq_with_heads_in_groups(B, H, T, D):
+    """A problem of eight or more rounds of workgroup slots runs dQ with its
+    heads in groups.  dQ of the whole launch must equal, bit for bit, dQ of
+    the same heads launched in batches small enough for the plain order (the
+    per-head arithmetic is the same, so any head missed, repeated or mixed
+    up by the grouped order shows), and heads at the group edges and inside
+    the groups are checked against the oracle."""
+    from oracle import attention as A
+    dev = need_gpu()
+    g = torch.Generator().manual_seed(11)
+    q, k, v, do = (torch.randn(B, H, T, D, generator=g).to(torch.bfloat16) for _ in range(4))
+    do = (do.float() * 0.01).to(torch.bfloat16)
+    sc = W.default_scale(D)
+    qd, kd, vd, dd = (t.to(dev) for t in (q, k, v, do))
+    o, lse = G.fwd(qd, kd, vd, sc)
+    dq, dk, dv = G.bwd(qd, kd, vd, o, dd, lse, sc)
+    torch.cuda.synchronize()
+    # the same heads in batches of at most 16 samples (at most two rounds)
+    step = 16
+    dq_parts = []
+    for b0 in range(0, B, step):
+        sl = slice(b0, b0 + step)
+        dqp, _, _ = G.bwd(qd[sl], kd[sl], vd[sl], o[sl], dd[sl], lse[sl], sc)
+        dq_parts.append(dqp)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, torch.cat(dq_parts)), "grouped dQ differs from the batched runs"
+    N = B * H
+    picks = sorted({0, N // 3 - 1, N // 3, N // 2 - 1, N // 2, 2 * N // 3, N - 1, 5 * N // 7})
+    for n in picks:
+        b, h = divmod(n, H)
+        ins = [t[b:b + 1, h:h + 1].double().numpy() for t in (q, k, v, do)]
+        ro, rl = A.forward(*ins[:3], sc)
+        rq, rk, rv = A.backward(*ins, sc)
+        got = {n_: to64(t[b:b + 1, h:h + 1]) for n_, t in
+               (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv))}
+        compare(got, {"o": ro, "lse": rl, "dq": rq, "dk": rk, "dv": rv}, "bf16",
+                label="heads in groups %s head %d" % ((B, H, T, D), n))
+
+
 def test_many_heads_large_grid():
     """32768 head-problems of 65 positions: a grid of 32768 workgroups per
     launch, every head computed; sampled heads checked against the oracle."""
