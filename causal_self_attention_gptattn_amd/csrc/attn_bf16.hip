@@ -32,10 +32,11 @@
 //                 dQ^T += K^T dS^T.
 //   attn_bwd_dq16 the same at D = 64 with 16 queries per wave on the
 //                 16 x 16 x 32 product (four waves per SIMD instead of three).
-//                 Both dQ kernels run longest query blocks first; a problem
-//                 of eight or more rounds of the GPU's workgroup slots takes
-//                 its heads in groups (grouped_item), so that each head's K/V
-//                 tiles are re-read close together in time and stay cached.
+//                 The forward and both dQ kernels run longest query blocks
+//                 first; a problem of eight or more rounds of the GPU's
+//                 workgroup slots takes its heads in groups (grouped_item;
+//                 the forward at D = 128 only), so that each head's K/V tiles
+//                 are re-read close together in time and stay cached.
 //   attn_bwd_dkdv16w  one workgroup = 64 keys of one head (4 waves x 16).
 //                 Walks the query tiles that see its keys with the
 //                 lane -> key layout: S = Q K^T and dP = dO V^T, then
@@ -187,7 +188,7 @@ __device__ __forceinline__ QItem grouped_item(int b, int N, int nqb, int hg) {
 template <int D, bool DROP>
 __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd(
     View Q, View K, View V, View O, float* __restrict__ LSE, Problem pb, int nqb, int deal,
-    int dealg) {
+    int dealg, int hg) {
   constexpr int BM = kBM, BN = kBN;
   constexpr int LD = D + 8;     // row stride of the epilogue staging (padded)
   constexpr int DS = D / 16;    // k-steps of the score product
@@ -205,10 +206,11 @@ __global__ __launch_bounds__(kThreads, D == 64 ? 4 : 2) void attn_fwd(
   SwzLane<D> sw;
   sw.init(c, g, tr_rowoff(lane), tr_coloff(lane));
   const int bid = blockIdx.x;
-  // longest query blocks first, dealt over the CUs
-  const int item = dealt_item(bid, nqb * pb.N, deal, dealg);
-  const int qb = nqb - 1 - item / pb.N;
-  const int n = item % pb.N;
+  // longest query blocks first (heads in groups on large problems), dealt
+  // over the CUs
+  const QItem qit = grouped_item(dealt_item(bid, nqb * pb.N, deal, dealg), pb.N, nqb, hg);
+  const int qb = qit.qb;
+  const int n = qit.n;
   const uint16_t* Kh = head_of(K, n, pb.H);
   const uint16_t* Vh = head_of(V, n, pb.H);
   const int q0 = qb * BM;
@@ -935,6 +937,19 @@ View view(const TensorArg& t) {
   return View{static_cast<const uint16_t*>(t.data), t.sb, t.sh, t.st};
 }
 
+// Heads per group for grouped_item: problems of at least eight rounds of the
+// GPU's workgroup slots (per_cu resident workgroups on each CU) take their
+// heads in balanced groups of about four rounds each, in multiples of 8
+// heads; smaller ones, and head counts that are not multiples of 8, run the
+// plain longest-first list (one group of all N heads).
+int head_group(int N, int nq, int cus, int per_cu) {
+  const long long slots = (long long)cus * per_cu;
+  if (slots <= 0 || N % 8 != 0 || (long long)N * nq < 8 * slots) return N;
+  const long long groups = ((long long)N * nq + 4 * slots - 1) / (4 * slots);
+  const long long h = ((N + groups - 1) / groups + 7) / 8 * 8;
+  return (int)(h < N ? h : N);
+}
+
 }  // namespace
 
 Problem make_problem(const ProblemArg& p) {
@@ -961,12 +976,15 @@ hipError_t launch_fwd_bf16(const TensorArg& q, const TensorArg& k, const TensorA
   const bool drop = p.dropout > 0.0f;
   // at D = 64 (four workgroups per CU) the longest-first list is dealt over
   // the CUs (dealt_item); at D = 128 it runs in list order
-  const int cus = p.D == 64 ? cu_count(stream) : 0;
-  const int deal = cus > 0 && cus % 8 == 0 ? cus : 0;
+  const int cus = cu_count(stream);
+  const int deal = p.D == 64 && cus > 0 && cus % 8 == 0 ? cus : 0;
   const int dealg = pb.N % 8 == 0 ? 8 : 1;
+  // heads in groups on large problems at D = 128 (at D = 64 the dealt order
+  // alone measured as fast: 1152 heads of 1024 tokens 251 against 258 us)
+  const int hg = p.D == 128 ? head_group(pb.N, nqb, cus, 2) : pb.N;
 #define GPTATTN_FWD(D_, DROP_)                                                                  \
   launch(attn_fwd<D_, DROP_>, blocks, stream, view(q), view(k), view(v), view(o), lse, pb, nqb, \
-         deal, dealg)
+         deal, dealg, hg)
   switch (p.D) {
     case 64: return drop ? GPTATTN_FWD(64, true) : GPTATTN_FWD(64, false);
     case 128: return drop ? GPTATTN_FWD(128, true) : GPTATTN_FWD(128, false);
@@ -983,24 +1001,15 @@ hipError_t launch_bwd_dq_bf16(const TensorArg& q, const TensorArg& k, const Tens
   const int nqb = (p.Tq + kBM - 1) / kBM;
   const long long blocks = (long long)pb.N * nqb;
   const bool drop = p.dropout > 0.0f;
-  // Problems of at least eight rounds of the GPU's workgroup slots take their
-  // heads in balanced groups of about four rounds each (multiples of 8
-  // heads); smaller ones run the plain longest-first list (one group).
+  // heads in groups on large problems (head_group)
   const int cus = cu_count(stream);
-  auto group_of = [&](int nq, int per_cu) {
-    const long long slots = (long long)cus * per_cu;
-    if (slots <= 0 || pb.N % 8 != 0 || (long long)pb.N * nq < 8 * slots) return pb.N;
-    const long long groups = ((long long)pb.N * nq + 4 * slots - 1) / (4 * slots);
-    const long long h = ((pb.N + groups - 1) / groups + 7) / 8 * 8;
-    return (int)(h < pb.N ? h : pb.N);
-  };
-  const int hg = group_of(nqb, 2);
+  const int hg = head_group(pb.N, nqb, cus, 2);
 #define GPTATTN_DQ(D_, DROP_)                                                                   \
   launch(attn_bwd_dq<D_, DROP_>, blocks, stream, view(q), view(k), view(v), view(o), view(dO),  \
          lse, view(dq), delta, pb, nqb, hg)
   const int nqb16 = (p.Tq + kBM16 - 1) / kBM16;
   const long long blocks16 = (long long)pb.N * nqb16;
-  const int hg16 = group_of(nqb16, 4);
+  const int hg16 = head_group(pb.N, nqb16, cus, 4);
 #define GPTATTN_DQ16(D_, DROP_)                                                                 \
   launch(attn_bwd_dq16<D_, DROP_>, blocks16, stream, view(q), view(k), view(v), view(o),        \
          view(dO), lse, view(dq), delta, pb, nqb16, hg16)
