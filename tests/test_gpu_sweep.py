@@ -121,16 +121,17 @@ def test_long_sequence_forward_rows(D):
 @pytest.mark.parametrize("B,H,T,D", [
     (48, 12, 1024, 64),   # 576 heads: 9 rounds of dQ's slots (dQ grouped, forward not)
     (96, 12, 1024, 64),   # 1152 heads: dQ grouped (the D = 64 forward keeps its dealt order)
-    (256, 8, 256, 128),   # 2048 heads: 8 rounds of the D = 128 kernels' slots (both grouped)
+    (256, 8, 256, 128),   # 2048 heads: 8 rounds of the forward's and dQ's slots, 16 of
+                          # dK/dV's (all three grouped)
 ])
 def test_heads_in_groups(B, H, T, D):
-    """A problem of eight or more rounds of workgroup slots runs dQ (and the
-    forward at D = 128) with its heads in groups.  O, lse and dQ of the whole
-    launch must equal, bit for bit, those of the same heads launched in
-    batches small enough for the plain order (the per-head arithmetic is the
-    same, so any head missed, repeated or mixed up by the grouped order
-    shows), and heads at the group edges and inside the groups are checked
-    against the oracle."""
+    """A problem of eight or more rounds of workgroup slots runs dQ (and, at
+    D = 128, the forward and dK/dV) with its heads in groups.  Every output
+    of the whole launch must equal, bit for bit, that of the same heads
+    launched in batches small enough for the plain order on the same kernels
+    (the per-head arithmetic is the same, so any head missed, repeated or
+    mixed up by the grouped order shows), and heads at the group edges and
+    inside the groups are checked against the oracle."""
     from oracle import attention as A
     dev = need_gpu()
     g = torch.Generator().manual_seed(11)
@@ -141,20 +142,19 @@ def test_heads_in_groups(B, H, T, D):
     o, lse = G.fwd(qd, kd, vd, sc)
     dq, dk, dv = G.bwd(qd, kd, vd, o, dd, lse, sc)
     torch.cuda.synchronize()
-    # the same heads in batches of at most 16 samples (at most two rounds)
-    step = 16
-    o_parts, lse_parts, dq_parts = [], [], []
+    # the same heads in batches of fewer rounds (plain order), large enough
+    # for the persistent dK/dV grid (more 128-key items than compute units)
+    step = 16 if D == 64 else 32
+    parts = {n_: [] for n_ in ("o", "lse", "dq", "dk", "dv")}
     for b0 in range(0, B, step):
         sl = slice(b0, b0 + step)
         op, lp = G.fwd(qd[sl], kd[sl], vd[sl], sc)
-        dqp, _, _ = G.bwd(qd[sl], kd[sl], vd[sl], o[sl], dd[sl], lse[sl], sc)
-        o_parts.append(op)
-        lse_parts.append(lp)
-        dq_parts.append(dqp)
+        dqp, dkp, dvp = G.bwd(qd[sl], kd[sl], vd[sl], o[sl], dd[sl], lse[sl], sc)
+        for n_, t in (("o", op), ("lse", lp), ("dq", dqp), ("dk", dkp), ("dv", dvp)):
+            parts[n_].append(t)
     torch.cuda.synchronize()
-    assert torch.equal(o, torch.cat(o_parts)), "grouped O differs from the batched runs"
-    assert torch.equal(lse, torch.cat(lse_parts)), "grouped lse differs from the batched runs"
-    assert torch.equal(dq, torch.cat(dq_parts)), "grouped dQ differs from the batched runs"
+    for n_, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv)):
+        assert torch.equal(t, torch.cat(parts[n_])), "grouped %s differs from the batched runs" % n_
     N = B * H
     picks = sorted({0, N // 3 - 1, N // 3, N // 2 - 1, N // 2, 2 * N // 3, N - 1, 5 * N // 7})
     for n in picks:
