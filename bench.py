@@ -688,6 +688,17 @@ def main():
         e[2].record(stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - t0
+
+    # warm steps: back to back, no flush, wall clock; right after the timed
+    # steps (after the clock sampling below, whose rocm-smi / amd-smi calls
+    # leave the next steps measurably slower, they read 0.1435 against
+    # 0.1338 ms for the flushed steps on one box)
+    tw = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize(dev)
+    warm_ms = (time.perf_counter() - tw) * 1e3 / args.steps
+
     # The clock under this load: rocm-smi polled while the same flushed steps
     # keep running right after the timed region (a rocm-smi call during the
     # timed steps stalls the step it lands on by half a millisecond, so it
@@ -706,14 +717,6 @@ def main():
     ms = float(step_ms.mean())
     value = flops / (ms * 1e-3) / 1e12
     q1, med, q3 = (float(x) for x in np.percentile(step_ms, [25, 50, 75]))
-
-    # warm steps: back to back, no flush, wall clock
-    torch.cuda.synchronize(dev)
-    tw = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize(dev)
-    warm_ms = (time.perf_counter() - tw) * 1e3 / args.steps
 
     rl = roofline(table[dom]["flops"], table[dom]["bytes"], dom_ms * 1e-3)
     kernels = {}
